@@ -1,0 +1,225 @@
+"""Exact tiled (fused) softmax attention for MI355X (gfx950).
+
+A thin ctypes binding over ``libattn.so`` (C ABI in ``include/attn.h``). This
+module only marshals arguments: it checks tensor shapes, dtypes and devices,
+allocates outputs with torch on the current device, and passes raw device
+pointers and the current HIP stream to the library. Every step of the
+computation runs in the library's HIP kernels; there is no fallback path, and
+the module raises if the library is missing or a call fails.
+
+    o, lse = fwd(q, k, v, causal=False, kv_len=None, dropout_p=0.0, seed=0,
+                 scale=None, out_dtype=None)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, <same keyword arguments>)
+    keep = dropout_mask(B, H, N, dropout_p, seed, device)
+
+Tensors are (B, H, N, d), contiguous, float16 or bfloat16, d in {64, 128}.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_F16, ATTN_BF16, ATTN_F32 = 0, 1, 2
+STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
+                3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_LAUNCH"}
+
+# Entry points declared in include/attn.h (checked by the ABI tests).
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_dropout_mask",
+           "attn_status_string", "attn_version")
+
+
+class AttnParams(ctypes.Structure):
+    """Mirror of attn_params in include/attn.h."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("kv_len", ctypes.c_void_p),
+        ("dropout_p", ctypes.c_float),
+        ("seed", ctypes.c_uint64),
+    ]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so and declare its signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m exact_tiled_attention_20_amd.build` "
+            "(the library has no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(AttnParams)
+    vp = ctypes.c_void_p
+    lib.attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_bytes.argtypes = [P]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_dropout_mask.argtypes = [P, vp, vp]
+    lib.attn_dropout_mask.restype = ctypes.c_int
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def make_params(B: int, H: int, N: int, d: int, *, dtype: int, out_dtype: int,
+                scale: float, causal: bool = False, kv_len_ptr: int = 0,
+                dropout_p: float = 0.0, seed: int = 0) -> AttnParams:
+    return AttnParams(int(B), int(H), int(N), int(d), int(dtype), int(out_dtype),
+                      float(scale), 1 if causal else 0,
+                      ctypes.c_void_p(kv_len_ptr or None), float(dropout_p),
+                      int(seed) & 0xFFFFFFFFFFFFFFFF)
+
+
+# --------------------------------------------------------------------------
+# torch-facing wrappers (torch provides device memory and the stream)
+
+def _torch():
+    import torch
+    return torch
+
+
+def _code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float16:
+        return ATTN_F16
+    if dt == torch.bfloat16:
+        return ATTN_BF16
+    if dt == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_qkv(q, k, v):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous (B, H, N, d) tensor")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have the same shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have the same dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+
+
+def _params_from(q, *, causal, kv_len, dropout_p, seed, scale, out_dtype):
+    torch = _torch()
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    odt = q.dtype if out_dtype is None else out_dtype
+    kv_ptr = 0
+    if kv_len is not None:
+        if kv_len.dtype != torch.int32 or kv_len.device != q.device or kv_len.numel() != B \
+                or not kv_len.is_contiguous():
+            raise ValueError("kv_len must be a contiguous int32 device tensor of B entries")
+        kv_ptr = kv_len.data_ptr()
+    p = make_params(B, H, N, d, dtype=_code(q.dtype), out_dtype=_code(odt), scale=scale,
+                    causal=causal, kv_len_ptr=kv_ptr, dropout_p=dropout_p, seed=seed)
+    return p, odt
+
+
+def fwd(q, k, v, *, causal: bool = False, kv_len=None, dropout_p: float = 0.0,
+        seed: int = 0, scale: Optional[float] = None, out_dtype=None,
+        out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Fused forward: returns (O, lse). O has out_dtype (default q.dtype)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    p, odt = _params_from(q, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
+                          scale=scale, out_dtype=out_dtype)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = lib.attn_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                      out.data_ptr(), lse.data_ptr(), _stream_ptr(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def bwd_workspace_bytes(q, *, causal=False, kv_len=None, dropout_p=0.0, seed=0,
+                        scale=None, out_dtype=None) -> int:
+    p, _ = _params_from(q, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
+                        scale=scale, out_dtype=out_dtype)
+    return int(load_library().attn_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None, dropout_p: float = 0.0,
+        seed: int = 0, scale: Optional[float] = None, out_dtype=None,
+        workspace=None):
+    """Fused backward with recomputation: returns (dQ, dK, dV) in out_dtype."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    if do.shape != q.shape or do.dtype != q.dtype or not do.is_contiguous():
+        raise ValueError("do must match q in shape and dtype and be contiguous")
+    p, odt = _params_from(q, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
+                          scale=scale, out_dtype=out_dtype)
+    if o.dtype != odt or o.shape != q.shape or not o.is_contiguous():
+        raise ValueError("o must be the forward output (same out_dtype and shape)")
+    if lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's float32 (B, H, N) statistic")
+    need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty(q.shape, dtype=odt, device=q.device)
+    dk = torch.empty(q.shape, dtype=odt, device=q.device)
+    dv = torch.empty(q.shape, dtype=odt, device=q.device)
+    st = lib.attn_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                      dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                      _stream_ptr(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def dropout_mask(B: int, H: int, N: int, dropout_p: float, seed: int, device,
+                 d: int = 64) -> "torch.Tensor":
+    """The raw Philox keep decisions, uint8 (B, H, N, N), as the kernels draw them."""
+    torch = _torch()
+    lib = load_library()
+    keep = torch.empty((B, H, N, N), dtype=torch.uint8, device=device)
+    p = make_params(B, H, N, d, dtype=ATTN_F16, out_dtype=ATTN_F16, scale=1.0,
+                    dropout_p=dropout_p, seed=seed)
+    st = lib.attn_dropout_mask(ctypes.byref(p), keep.data_ptr(), _stream_ptr(device))
+    if st != 0:
+        raise AttnError(st, "attn_dropout_mask")
+    return keep

@@ -1,0 +1,220 @@
+// Host side of the C ABI declared in include/attn.h.
+//
+// Every argument is validated here, on the host, before any HIP call; an
+// unsupported combination returns ATTN_ERR_UNSUPPORTED and nothing runs. The
+// anthology-of-the-sota page SOTA-114 ("Cost") names the hazard this avoids:
+// fused kernels exist per (mask, dropout, head dim, dtype) combination and a
+// silent fallback to a slow path goes unnoticed. This library has no fallback.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(int32_t dt) { return dt == ATTN_F32 ? 4 : 2; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlap(Range x, Range y) { return x.lo < y.hi && y.lo < x.hi; }
+
+// Shape/dtype/scalar checks common to every entry point.
+attn_status check_params(const attn_params* p) {
+  if (p == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (p->B < 1 || p->H < 1 || p->N < 1 || p->d < 1) return ATTN_ERR_INVALID_ARG;
+  if (p->dtype != ATTN_F16 && p->dtype != ATTN_BF16 && p->dtype != ATTN_F32)
+    return ATTN_ERR_INVALID_ARG;
+  if (p->out_dtype != ATTN_F16 && p->out_dtype != ATTN_BF16 && p->out_dtype != ATTN_F32)
+    return ATTN_ERR_INVALID_ARG;
+  if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(p->scale) || p->scale == 0.0f) return ATTN_ERR_INVALID_ARG;
+  if (!(p->dropout_p >= 0.0f && p->dropout_p < 1.0f)) return ATTN_ERR_INVALID_ARG;
+  // Element counts: per head N*d must index in 32 bits; the whole tensor must
+  // stay far from overflow of 64-bit byte offsets; the grids must fit.
+  const long long per_head = (long long)p->N * p->d;
+  if (per_head >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  const long long heads = (long long)p->B * p->H;
+  if (heads >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  if ((double)heads * (double)per_head >= 4.0e18) return ATTN_ERR_INVALID_ARG;
+  const long long blocks = heads * ((p->N + attn::kFwdBlockQ - 1) / attn::kFwdBlockQ);
+  if (blocks + 8 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  // Supported kernels.
+  if (p->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (p->out_dtype != p->dtype && p->out_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (p->d != 64 && p->d != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+uint32_t drop_threshold(float p) {
+  // floor(p * 2^32) is exact in double for a float p in [0, 1).
+  return (uint32_t)std::floor((double)p * 4294967296.0);
+}
+
+size_t tensor_bytes(const attn_params* p, int32_t dt) {
+  return (size_t)p->B * p->H * p->N * p->d * elem_bytes(dt);
+}
+
+size_t stat_bytes(const attn_params* p) { return (size_t)p->B * p->H * p->N * sizeof(float); }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK: success";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument (pointer, size, scale, p or flag)";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: no kernel for this head dimension / dtype combination";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: backward workspace missing, misaligned or too small";
+    case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+  }
+  return "unknown attn_status";
+}
+
+int32_t attn_version(void) { return kVersion; }
+
+attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
+                     void* o, float* lse, void* stream) {
+  attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* x : ptrs)
+    if (x == nullptr || !aligned16(x)) return ATTN_ERR_INVALID_ARG;
+  const size_t in_b = tensor_bytes(p, p->dtype);
+  const Range outs[] = {range_of(o, tensor_bytes(p, p->out_dtype)), range_of(lse, stat_bytes(p))};
+  const Range ins[] = {range_of(q, in_b), range_of(k, in_b), range_of(v, in_b)};
+  if (overlap(outs[0], outs[1])) return ATTN_ERR_INVALID_ARG;
+  for (const Range& r : outs)
+    for (const Range& x : ins)
+      if (overlap(r, x)) return ATTN_ERR_INVALID_ARG;
+  if (p->kv_len != nullptr && (reinterpret_cast<uintptr_t>(p->kv_len) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+
+  attn::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.lse = lse;
+  a.kv_len = p->kv_len;
+  a.B = p->B;
+  a.H = p->H;
+  a.N = p->N;
+  a.nqb = (p->N + attn::kFwdBlockQ - 1) / attn::kFwdBlockQ;
+  a.total = p->B * p->H * a.nqb;
+  a.per_xcd = (a.total + 7) / 8;
+  a.scale = p->scale;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  const bool dropout = p->dropout_p > 0.0f;
+  a.drop_threshold = drop_threshold(p->dropout_p);
+  a.drop_rescale = 1.0f / (1.0f - p->dropout_p);
+  a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
+  a.seed_hi = (uint32_t)(p->seed >> 32);
+  const hipError_t e = attn::launch_fwd(p->dtype == ATTN_BF16 ? 1 : 0, p->d, p->causal != 0,
+                                        dropout, p->out_dtype == ATTN_F32, a,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t attn_bwd_workspace_bytes(const attn_params* p) {
+  if (check_params(p) != ATTN_OK) return 0;
+  // D_i = dO_i . O_i in fp32, (B, H, N), rounded up to 256 bytes.
+  return (stat_bytes(p) + 255) & ~size_t(255);
+}
+
+attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                     void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  const void* ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
+  for (const void* x : ptrs)
+    if (x == nullptr || !aligned16(x)) return ATTN_ERR_INVALID_ARG;
+  if (p->kv_len != nullptr && (reinterpret_cast<uintptr_t>(p->kv_len) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn_bwd_workspace_bytes(p);
+  if (workspace == nullptr || workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return ATTN_ERR_WORKSPACE;
+  const size_t in_b = tensor_bytes(p, p->dtype);
+  const size_t out_b = tensor_bytes(p, p->out_dtype);
+  const Range outs[] = {range_of(dq, out_b), range_of(dk, out_b), range_of(dv, out_b),
+                        range_of(workspace, need)};
+  const Range ins[] = {range_of(q, in_b), range_of(k, in_b), range_of(v, in_b),
+                       range_of(o, out_b), range_of(lse, stat_bytes(p)), range_of(d_o, in_b)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return ATTN_ERR_INVALID_ARG;
+    for (const Range& x : ins)
+      if (overlap(outs[i], x)) return ATTN_ERR_INVALID_ARG;
+  }
+
+  attn::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.lse = lse;
+  a.d_o = static_cast<const uint16_t*>(d_o);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  a.kv_len = p->kv_len;
+  a.B = p->B;
+  a.H = p->H;
+  a.N = p->N;
+  a.nkb = (p->N + attn::kBwdBlockK - 1) / attn::kBwdBlockK;
+  a.nqb = (p->N + attn::kBwdBlockQ - 1) / attn::kBwdBlockQ;
+  a.per_xcd_k = (p->B * p->H * a.nkb + 7) / 8;
+  a.per_xcd_q = (p->B * p->H * a.nqb + 7) / 8;
+  a.scale = p->scale;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  const bool dropout = p->dropout_p > 0.0f;
+  a.drop_threshold = drop_threshold(p->dropout_p);
+  a.drop_rescale = 1.0f / (1.0f - p->dropout_p);
+  a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
+  a.seed_hi = (uint32_t)(p->seed >> 32);
+  const hipError_t e = attn::launch_bwd(p->dtype == ATTN_BF16 ? 1 : 0, p->d, p->causal != 0,
+                                        dropout, p->out_dtype == ATTN_F32, a,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream) {
+  attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  if (keep == nullptr || !aligned16(keep)) return ATTN_ERR_INVALID_ARG;
+  const double cells = (double)p->B * p->H * p->N * (double)p->N;
+  if (cells >= 9.0e15) return ATTN_ERR_INVALID_ARG;
+  attn::MaskArgs a;
+  a.keep = keep;
+  a.B = p->B;
+  a.H = p->H;
+  a.N = p->N;
+  a.drop_threshold = drop_threshold(p->dropout_p);
+  a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
+  a.seed_hi = (uint32_t)(p->seed >> 32);
+  const long long groups = (long long)p->B * p->H * p->N * ((p->N + 3) / 4);
+  if ((groups + 255) / 256 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_dropout_mask(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

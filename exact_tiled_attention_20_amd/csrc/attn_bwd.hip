@@ -1,0 +1,554 @@
+// Fused attention backward for gfx950, recomputing scores from the saved
+// log-sum-exp ("Why FlashAttention Is a Kernel Story", section "When it falls
+// down", backward pass: S and P are not stored by the forward and are rebuilt
+// from the output and the log-sum-exp).
+//
+// With P_ij = exp(scale * Q_i.K_j - lse_i) on visible pairs, Z_ij the dropout
+// factor (keep / (1-p), or 1), and D_i = dO_i . O_i:
+//     dV_j = sum_i P_ij Z_ij dO_i
+//     dP_ij = Z_ij dO_i . V_j,   dS_ij = P_ij (dP_ij - D_i)
+//     dK_j = scale * sum_i dS_ij Q_i,   dQ_i = scale * sum_j dS_ij K_j
+//
+// Three kernels on the caller's stream:
+//   1. preprocess: D_i for every row (HBM-bound, 16 lanes per row).
+//   2. dK/dV: one workgroup per 128 keys (4 waves x 32 keys). K and V stay in
+//      VGPRs as MFMA B operands; Q, dO, lse and D stream through LDS in tiles of
+//      64 queries. Scores are computed as S = Q K^T so that each lane owns one
+//      key and the query index runs along the accumulator registers: the fp32
+//      registers of P and dS, rounded to the input dtype, are then directly the
+//      A operands of dV = P^T dO and dK = dS^T Q, and dO and Q are fed as B
+//      operands by ds_read_b64_tr_b16 from their row-major LDS tiles.
+//   3. dQ: one workgroup per 128 queries (4 waves x 32 queries), the forward's
+//      orientation (S^T = K Q^T, one query per lane) plus dP^T = V dO^T; dQ^T =
+//      K^T dS^T reads K transposed from LDS. Deterministic: no atomics.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <bool OUT_F32, typename E>
+__device__ __forceinline__ float load_out(const void* p, size_t idx) {
+  if (OUT_F32) return ((const float*)p)[idx];
+  return E::to_float(((const uint16_t*)p)[idx]);
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dO[i][c] * O[i][c]. D/8 lanes per row, 8 elements per lane.
+template <typename E, int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs a) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const long long rows = (long long)a.B * a.H * a.N;
+  const long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const size_t base = (size_t)row * D + part * 8;
+    const u32x4 g = *(const u32x4*)(a.d_o + base);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float g0 = E::to_float((uint16_t)(g[e] & 0xFFFF));
+      const float g1 = E::to_float((uint16_t)(g[e] >> 16));
+      acc = __builtin_fmaf(g0, load_out<OUT_F32, E>(a.o, base + 2 * e), acc);
+      acc = __builtin_fmaf(g1, load_out<OUT_F32, E>(a.o, base + 2 * e + 1), acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && part == 0) a.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV. Workgroup: 128 keys of one (b, h); wave w owns keys kw .. kw+31.
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr int BKW = 128;             // keys per workgroup
+  constexpr int BQ = kBwdBlockQ;       // queries per LDS tile (2 sub-blocks of 32)
+  constexpr int KK = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int TILE_BYTES = BQ * D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = BQ * CPR / kBwdThreads;
+  static_assert(CPT >= 1, "tile too small");
+
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
+  __shared__ __attribute__((aligned(16))) float s_del[2][BQ];
+
+  const int nkb = (a.N + BKW - 1) / BKW;
+  const int total = a.B * a.H * nkb;
+  const int per_xcd = (total + 7) / 8;
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= total) return;
+  const int bh = item / nkb;
+  const int kblk = item - bh * nkb;    // ascending: heaviest first under causal
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  const int N = a.N;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* __restrict__ Q = a.q + head;
+  const uint16_t* __restrict__ K = a.k + head;
+  const uint16_t* __restrict__ V = a.v + head;
+  const uint16_t* __restrict__ dO = a.d_o + head;
+  const float* __restrict__ LSE = a.lse + (size_t)bh * N;
+  const float* __restrict__ DEL = a.delta + (size_t)bh * N;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int k0 = kblk * BKW;
+  const int kw = k0 + 32 * w;
+  const int j = kw + l32;              // this lane's key
+
+  int kv_end = N;
+  if (a.kv_len != nullptr) kv_end = min(max(a.kv_len[b], 0), N);
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.f;
+      dv[db][r] = 0.f;
+    }
+
+  if (k0 < kv_end) {
+    // K and V rows of this lane's key as B operands (K^T, V^T columns).
+    u32x4 kf[KK], vf[KK];
+    {
+      const int jr = min(j, N - 1);
+      const uint16_t* ks = K + (size_t)jr * D + hh * 8;
+      const uint16_t* vs = V + (size_t)jr * D + hh * 8;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        kf[kk] = *(const u32x4*)(ks + kk * 16);
+        vf[kk] = *(const u32x4*)(vs + kk * 16);
+      }
+    }
+    const bool wave_has_keys = kw < kv_end;
+    const int qt0 = CAUSAL ? (k0 / BQ) : 0;
+    const int nqt = (N + BQ - 1) / BQ;
+    char* const qb0 = smem;
+    char* const ob0 = smem + 2 * TILE_BYTES;
+
+    u32x4 qr[CPT], orr[CPT];
+    float lse_r = 0.f, del_r = 0.f;
+    auto load_tile = [&](int t) {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int id = tid + kBwdThreads * u;
+        const int row = id / CPR;
+        const int c = id - row * CPR;
+        const int qi = t * BQ + row;
+        if (qi < N) {
+          qr[u] = *(const u32x4*)(Q + (size_t)qi * D + c * 8);
+          orr[u] = *(const u32x4*)(dO + (size_t)qi * D + c * 8);
+        } else {
+          qr[u] = u32x4{0, 0, 0, 0};
+          orr[u] = u32x4{0, 0, 0, 0};
+        }
+      }
+      if (tid < BQ) {
+        const int qi = t * BQ + tid;
+        // Rows past N or with no visible key contribute nothing: P = 0.
+        float ls = INFINITY, dl = 0.f;
+        if (qi < N) {
+          const float x = LSE[qi];
+          ls = (x == -INFINITY) ? INFINITY : x * kLog2e;
+          dl = DEL[qi];
+        }
+        lse_r = ls;
+        del_r = dl;
+      }
+    };
+    auto store_tile = [&](int buf) {
+      char* qb = qb0 + buf * TILE_BYTES;
+      char* ob = ob0 + buf * TILE_BYTES;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int id = tid + kBwdThreads * u;
+        const int row = id / CPR;
+        const int c = id - row * CPR;
+        *(u32x4*)(qb + lds_off<D>(row, c * 16)) = qr[u];
+        *(u32x4*)(ob + lds_off<D>(row, c * 16)) = orr[u];
+      }
+      if (tid < BQ) {
+        s_lse[buf][tid] = lse_r;
+        s_del[buf][tid] = del_r;
+      }
+    };
+
+    const float c2 = a.scale_log2;
+    if (qt0 < nqt) {
+      load_tile(qt0);
+      store_tile(0);
+    }
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    for (int t = qt0; t < nqt; ++t) {
+      __syncthreads();
+      const int buf = (t - qt0) & 1;
+      const bool more = (t + 1) < nqt;
+      if (more) load_tile(t + 1);
+      const char* qb = qb0 + buf * TILE_BYTES;
+      const char* ob = ob0 + buf * TILE_BYTES;
+#pragma unroll
+      for (int sub = 0; sub < BQ / 32; ++sub) {
+        const int qbase = t * BQ + 32 * sub;
+        const bool active = wave_has_keys && qbase < N && (!CAUSAL || qbase + 31 >= kw);
+        if (!active) continue;
+        // S = Q K^T and dP = dO V^T (32 queries x 32 keys), lane = key.
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] = 0.f;
+          dp[r] = 0.f;
+        }
+        const int row = 32 * sub + l32;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 qa = *(const u32x4*)(qb + lds_off<D>(row, (kk * 2 + hh) * 16));
+          s = E::mfma(qa, kf[kk], s);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 oa = *(const u32x4*)(ob + lds_off<D>(row, (kk * 2 + hh) * 16));
+          dp = E::mfma(oa, vf[kk], dp);
+        }
+        // P, dropout, dS. Register r holds query qbase + 8(r/4) + 4hh + r%4.
+        f32x16 pz, ds;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int ql = 32 * sub + 8 * g4 + 4 * hh;
+          const f32x4 ls4 = *(const f32x4*)&s_lse[buf][ql];
+          const f32x4 dl4 = *(const f32x4*)&s_del[buf][ql];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            const int qi = qbase + 8 * g4 + 4 * hh + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[e]));
+            const bool dead = (CAUSAL && j > qi) || (j >= kv_end);
+            if (dead) p = 0.f;
+            float z = 1.f;
+            if (DROPOUT) {
+              const u32x4 u = dropout_draws((uint32_t)j >> 2, (uint32_t)qi, (uint32_t)h,
+                                            (uint32_t)b, a.seed_lo, a.seed_hi);
+              z = (u[j & 3] >= a.drop_threshold) ? a.drop_rescale : 0.f;
+            }
+            pz[r] = p * z;
+            ds[r] = p * (dp[r] * z - dl4[e]);
+          }
+        }
+        // dV += (P Z)^T dO and dK += dS^T Q; 16 queries per MFMA step.
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          u32x4 pa, sa;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pa[e] = E::pack2(pz[8 * c + 2 * e], pz[8 * c + 2 * e + 1]);
+            sa[e] = E::pack2(ds[8 * c + 2 * e], ds[8 * c + 2 * e + 1]);
+          }
+          const int row1 = 32 * sub + 16 * c + 4 * hh + (i16 >> 2);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int byte = (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2;
+            u32x4 ob4, qb4;
+            {
+              const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(ob, lds_off<D>(row1, byte)));
+              const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(ob, lds_off<D>(row1 + 8, byte)));
+              ob4 = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+            {
+              const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(qb, lds_off<D>(row1, byte)));
+              const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(qb, lds_off<D>(row1 + 8, byte)));
+              qb4 = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+            dv[db] = E::mfma(pa, ob4, dv[db]);
+            dk[db] = E::mfma(sa, qb4, dk[db]);
+          }
+        }
+      }
+      if (more) store_tile(buf ^ 1);
+    }
+  }
+
+  // Write dK (times scale) and dV: lane holds column 32db + l32 of key rows
+  // kw + 8(r/4) + 4hh + r%4.
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (key < N) {
+        const size_t idx = head + (size_t)key * D + 32 * db + l32;
+        const float gk = dk[db][r] * a.scale;
+        const float gv = dv[db][r];
+        if (OUT_F32) {
+          ((float*)a.dk)[idx] = gk;
+          ((float*)a.dv)[idx] = gv;
+        } else {
+          ((typename E::scalar*)a.dk)[idx] = (typename E::scalar)gk;
+          ((typename E::scalar*)a.dv)[idx] = (typename E::scalar)gv;
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ. Workgroup: 128 queries of one (b, h); wave w owns 32 query rows.
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dq_kernel(const BwdArgs a) {
+  constexpr int BR = 128;
+  constexpr int BC = 64;
+  constexpr int KK = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int NKB = BC / 32;
+  constexpr int NC16 = BC / 16;
+  constexpr int TILE_BYTES = BC * D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = BC * CPR / kBwdThreads;
+
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
+
+  const int nqb = (a.N + BR - 1) / BR;
+  const int total = a.B * a.H * nqb;
+  const int per_xcd = (total + 7) / 8;
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= total) return;
+  const int bh = item / nqb;
+  int qblk = item - bh * nqb;
+  if (CAUSAL) qblk = nqb - 1 - qblk;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  const int N = a.N;
+  const int q0 = qblk * BR;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* __restrict__ Q = a.q + head;
+  const uint16_t* __restrict__ K = a.k + head;
+  const uint16_t* __restrict__ V = a.v + head;
+  const uint16_t* __restrict__ dO = a.d_o + head;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  int kv_end = N;
+  if (a.kv_len != nullptr) kv_end = min(max(a.kv_len[b], 0), N);
+  int kend = kv_end;
+  if (CAUSAL) kend = min(kend, q0 + BR);
+  const int ntiles = (kend + BC - 1) / BC;
+
+  const int wq0 = q0 + 32 * w;
+  const int qi = wq0 + l32;
+  const bool wave_has_rows = wq0 < N;
+
+  u32x4 qf[KK], of[KK];
+  float lse2 = INFINITY, dlt = 0.f;
+  {
+    const int qr = min(qi, N - 1);
+    const uint16_t* qs = Q + (size_t)qr * D + hh * 8;
+    const uint16_t* os = dO + (size_t)qr * D + hh * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qf[kk] = *(const u32x4*)(qs + kk * 16);
+      of[kk] = *(const u32x4*)(os + kk * 16);
+    }
+    if (qi < N) {
+      const float x = a.lse[(size_t)bh * N + qi];
+      lse2 = (x == -INFINITY) ? INFINITY : x * kLog2e;
+      dlt = a.delta[(size_t)bh * N + qi];
+    }
+  }
+
+  char* const kb0 = smem;
+  char* const vb0 = smem + 2 * TILE_BYTES;
+  u32x4 kr[CPT], vr[CPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int id = tid + kBwdThreads * u;
+      const int row = id / CPR;
+      const int c = id - row * CPR;
+      const int key = t * BC + row;
+      if (key < kv_end) {
+        kr[u] = *(const u32x4*)(K + (size_t)key * D + c * 8);
+        vr[u] = *(const u32x4*)(V + (size_t)key * D + c * 8);
+      } else {
+        kr[u] = u32x4{0, 0, 0, 0};
+        vr[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* kb = kb0 + buf * TILE_BYTES;
+    char* vb = vb0 + buf * TILE_BYTES;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int id = tid + kBwdThreads * u;
+      const int row = id / CPR;
+      const int c = id - row * CPR;
+      *(u32x4*)(kb + lds_off<D>(row, c * 16)) = kr[u];
+      *(u32x4*)(vb + lds_off<D>(row, c * 16)) = vr[u];
+    }
+  };
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  const float c2 = a.scale_log2;
+  const int g = lane >> 4;
+  const int i16 = lane & 15;
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    const int buf = t & 1;
+    const bool more = (t + 1) < ntiles;
+    if (more) load_tile(t + 1);
+    const int k0 = t * BC;
+    const bool active = wave_has_rows && (!CAUSAL || k0 <= wq0 + 31);
+    if (active) {
+      const char* kb = kb0 + buf * TILE_BYTES;
+      const char* vb = vb0 + buf * TILE_BYTES;
+      f32x16 s[NKB], dp[NKB];
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[kb2][r] = 0.f;
+          dp[kb2][r] = 0.f;
+        }
+        const int row = kb2 * 32 + l32;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 ka = *(const u32x4*)(kb + lds_off<D>(row, (kk * 2 + hh) * 16));
+          s[kb2] = E::mfma(ka, qf[kk], s[kb2]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 va = *(const u32x4*)(vb + lds_off<D>(row, (kk * 2 + hh) * 16));
+          dp[kb2] = E::mfma(va, of[kk], dp[kb2]);
+        }
+      }
+      // dS^T = P^T (Z dP^T - D); register r of block kb2 is key
+      // k0 + 32kb2 + 8(r/4) + 4hh + r%4 of this lane's query row.
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int j0 = k0 + kb2 * 32 + 8 * g4 + 4 * hh;
+          u32x4 u = u32x4{0, 0, 0, 0};
+          if (DROPOUT)
+            u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h, (uint32_t)b,
+                              a.seed_lo, a.seed_hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            const int jj = j0 + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c2, -lse2));
+            if ((CAUSAL && jj > qi) || jj >= kv_end) p = 0.f;
+            float z = 1.f;
+            if (DROPOUT) z = (u[e] >= a.drop_threshold) ? a.drop_rescale : 0.f;
+            s[kb2][r] = p * (dp[kb2][r] * z - dlt);
+          }
+        }
+      // dQ^T += K^T dS^T, 16 keys per MFMA step; K read transposed from LDS.
+#pragma unroll
+      for (int c = 0; c < NC16; ++c) {
+        const int kb2 = c >> 1;
+        const int rr = (c & 1) * 8;
+        u32x4 sb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sb[e] = E::pack2(s[kb2][rr + 2 * e], s[kb2][rr + 2 * e + 1]);
+        const int row1 = c * 16 + 4 * hh + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int byte = (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2;
+          const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(kb, lds_off<D>(row1, byte)));
+          const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(kb, lds_off<D>(row1 + 8, byte)));
+          acc[db] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sb, acc[db]);
+        }
+      }
+    }
+    if (more) store_tile(buf ^ 1);
+  }
+
+  if (qi < N) {
+    const size_t orow = head + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dcol = 32 * db + 8 * g4 + 4 * hh;
+        const float v0 = acc[db][4 * g4 + 0] * a.scale;
+        const float v1 = acc[db][4 * g4 + 1] * a.scale;
+        const float v2 = acc[db][4 * g4 + 2] * a.scale;
+        const float v3 = acc[db][4 * g4 + 3] * a.scale;
+        if (OUT_F32) {
+          *(f32x4*)((float*)a.dq + orow + dcol) = f32x4{v0, v1, v2, v3};
+        } else {
+          *(u32x2*)((uint16_t*)a.dq + orow + dcol) = u32x2{E::pack2(v0, v1), E::pack2(v2, v3)};
+        }
+      }
+  }
+}
+
+template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
+static hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
+  const long long rows = (long long)a.B * a.H * a.N;
+  const long long threads = rows * (D / 8);
+  hipLaunchKernelGGL((attn_bwd_preprocess_kernel<E, D, OUT_F32>),
+                     dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkb = (a.N + 127) / 128;
+  const int tk = a.B * a.H * nkb;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>),
+                     dim3(((tk + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqb = (a.N + 127) / 128;
+  const int tq = a.B * a.H * nqb;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>),
+                     dim3(((tq + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t launch_d(bool causal, bool dropout, bool out_f32, const BwdArgs& a,
+                           hipStream_t s) {
+  if (causal) {
+    if (dropout) return out_f32 ? launch_all<E, D, true, true, true>(a, s)
+                                : launch_all<E, D, true, true, false>(a, s);
+    return out_f32 ? launch_all<E, D, true, false, true>(a, s)
+                   : launch_all<E, D, true, false, false>(a, s);
+  }
+  if (dropout) return out_f32 ? launch_all<E, D, false, true, true>(a, s)
+                              : launch_all<E, D, false, true, false>(a, s);
+  return out_f32 ? launch_all<E, D, false, false, true>(a, s)
+                 : launch_all<E, D, false, false, false>(a, s);
+}
+
+hipError_t launch_bwd(int dtype, int d, bool causal, bool dropout, bool out_f32,
+                      const BwdArgs& a, hipStream_t stream) {
+  if (dtype == 1) {
+    if (d == 128) return launch_d<Elem<bf16_t>, 128>(causal, dropout, out_f32, a, stream);
+    return launch_d<Elem<bf16_t>, 64>(causal, dropout, out_f32, a, stream);
+  }
+  if (d == 128) return launch_d<Elem<f16_t>, 128>(causal, dropout, out_f32, a, stream);
+  return launch_d<Elem<f16_t>, 64>(causal, dropout, out_f32, a, stream);
+}
+
+}  // namespace attn

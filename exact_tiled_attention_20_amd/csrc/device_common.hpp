@@ -1,0 +1,139 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Everything here is written for CDNA4 (gfx950) wave64 execution:
+//   * MFMA wrappers for v_mfma_f32_32x32x16_{bf16,f16}. Lane layouts (checked
+//     on the device): A operand, lane l holds A[l%32][8*(l/32) .. +8];
+//     B operand, lane l holds B[8*(l/32) .. +8][l%32]; the 32x32 fp32 result
+//     is spread so that lane l holds column l%32 and, in register r, row
+//     8*(r/4) + 4*(l/32) + r%4.
+//   * ds_read_b64_tr_b16 (LDS transpose read): within each group of 16 lanes,
+//     lane i receives element (i%4) of the 4-element rows addressed by lanes
+//     i/4, i/4+4, i/4+8, i/4+12 of its group.
+//   * Philox4x32-10 written from its published definition (Salmon, Moraes,
+//     Dror, Shaw, SC'11).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Storage element tags. Both are 16-bit in memory.
+struct bf16_t {};
+struct f16_t {};
+
+template <typename E> struct Elem;
+template <> struct Elem<bf16_t> {
+  typedef bf16x8 vec8;
+  typedef __bf16 scalar;
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Round-to-nearest-even pack of two floats into one dword (lo, hi).
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  static __device__ __forceinline__ float to_float(uint16_t x) {
+    return __uint_as_float((uint32_t)x << 16);
+  }
+};
+template <> struct Elem<f16_t> {
+  typedef f16x8 vec8;
+  typedef _Float16 scalar;
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  static __device__ __forceinline__ float to_float(uint16_t x) {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (SC'11): two multiplier rounds per step, Weyl key schedule.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    const uint32_t hi0 = __umulhi(kPhiloxM0, c[0]);
+    const uint32_t lo0 = kPhiloxM0 * c[0];
+    const uint32_t hi1 = __umulhi(kPhiloxM1, c[2]);
+    const uint32_t lo1 = kPhiloxM1 * c[2];
+    u32x4 n;
+    n[0] = hi1 ^ c[1] ^ k0;
+    n[1] = lo1;
+    n[2] = hi0 ^ c[3] ^ k1;
+    n[3] = lo0;
+    c = n;
+  }
+  return c;
+}
+
+// Draws for keys 4t..4t+3 of query i in head (b, h): counter (t, i, h, b).
+__device__ __forceinline__ u32x4 dropout_draws(uint32_t t, uint32_t i, uint32_t h,
+                                               uint32_t b, uint32_t k0, uint32_t k1) {
+  u32x4 c;
+  c[0] = t;
+  c[1] = i;
+  c[2] = h;
+  c[3] = b;
+  return philox4x32_10(c, k0, k1);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile layout. A tile is ROWS x D 16-bit elements, one row per key (or per
+// query), D*2 bytes per row. Tiles are read two ways:
+//   * row reads (MFMA A operands): 32 consecutive rows, one 16-byte chunk each;
+//   * transpose reads (ds_read_b64_tr_b16): per 32 lanes, 4 consecutive rows
+//     (starting at a multiple of 4) x 64 contiguous bytes.
+// The 16-byte chunk index is XORed with a row-dependent mask whose two high
+// bits rotate the 64-byte segment with row%4 and whose two low bits take the
+// next row bits, so both patterns touch every bank once per 256 bytes.
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int byte_in_row) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row: 16 (D=128) or 8 (D=64)
+  int sw;
+  if (D == 128)
+    sw = ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    sw = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  const int chunk = (byte_in_row >> 4) ^ sw;
+  return row * (D * 2) + ((chunk & (CPR - 1)) << 4) + (byte_in_row & 15);
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_base, int byte_off) {
+  const char* p = (const char*)lds_base + byte_off;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ float wave_swap_halves(float x) {
+  // Exchange with the lane 32 positions away (lanes 0..31 <-> 32..63).
+  return __shfl_xor(x, 32, 64);
+}
+
+}  // namespace attn

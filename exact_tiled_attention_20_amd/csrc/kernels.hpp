@@ -1,0 +1,78 @@
+// Launch descriptors shared between the host API and the gfx950 kernels.
+// Host code fills these after validating the caller's attn_params; kernels
+// receive them by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Forward tiling: 4 waves x 32 query rows per workgroup, 64 keys per tile.
+constexpr int kFwdBlockQ = 128;
+constexpr int kFwdBlockK = 64;
+constexpr int kFwdThreads = 256;
+
+// Backward tiling (dK/dV: 64 keys per workgroup; dQ: 128 queries per workgroup).
+constexpr int kBwdBlockK = 64;
+constexpr int kBwdBlockQ = 64;
+constexpr int kBwdThreads = 256;
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;               // out dtype: 16-bit storage or float
+  float* lse;
+  const int32_t* kv_len; // device [B] or nullptr
+  int B, H, N;
+  int nqb;               // query blocks per head
+  int per_xcd;           // work items per XCD (ceil(total / 8))
+  int total;             // B * H * nqb
+  float scale;           // softmax scale (fp32)
+  float scale_log2;      // scale * log2(e)
+  uint32_t drop_threshold;  // keep iff draw >= threshold
+  float drop_rescale;       // 1 / (1 - p)
+  uint32_t seed_lo, seed_hi;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* o;         // out dtype
+  const float* lse;
+  const uint16_t* d_o;
+  void* dq;              // out dtype
+  void* dk;
+  void* dv;
+  float* delta;          // workspace: D_i = dO_i . O_i, (B, H, N) fp32
+  const int32_t* kv_len;
+  int B, H, N;
+  int nkb;               // key blocks per head (dK/dV kernel)
+  int nqb;               // query blocks per head (dQ kernel)
+  int per_xcd_k;
+  int per_xcd_q;
+  float scale;
+  float scale_log2;
+  uint32_t drop_threshold;
+  float drop_rescale;
+  uint32_t seed_lo, seed_hi;
+};
+
+struct MaskArgs {
+  uint8_t* keep;
+  int B, H, N;
+  uint32_t drop_threshold;
+  uint32_t seed_lo, seed_hi;
+};
+
+// Kernel families. `dtype` is 0 (fp16) or 1 (bf16); `out_f32` selects float
+// outputs. Each returns hipSuccess or the launch error.
+hipError_t launch_fwd(int dtype, int d, bool causal, bool dropout, bool out_f32,
+                      const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(int dtype, int d, bool causal, bool dropout, bool out_f32,
+                      const BwdArgs& a, hipStream_t stream);
+hipError_t launch_dropout_mask(const MaskArgs& a, hipStream_t stream);
+
+}  // namespace attn

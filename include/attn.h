@@ -1,0 +1,128 @@
+/*
+ * attn.h -- C ABI of the exact tiled attention library for MI355X (gfx950).
+ *
+ * The operation is exact softmax attention,
+ *
+ *     O = softmax(scale * Q K^T + mask) V      (dropout on the probabilities),
+ *
+ * computed as one fused, tiled kernel: a block of Q rows stays on chip while
+ * blocks of K and V stream through, a running row maximum m and denominator l
+ * are updated per block (the online softmax), O is rescaled and accumulated,
+ * and only O and the per-row log-sum-exp are written. No N x N matrix reaches
+ * device memory. The backward pass recomputes the scores and probabilities
+ * from Q, K and the saved log-sum-exp.
+ *
+ * Sources (web pages on the method):
+ *   - "Why FlashAttention Is a Kernel Story" (praveentn.live), sections
+ *     "The real bottleneck" (the unfused chain and its memory traffic),
+ *     "Tiling: fitting the work inside SRAM" (the online-softmax update, the
+ *     final O / l, and the O(Nd) traffic), "Why this only works as a fused
+ *     kernel", and "When it falls down" (backward recomputation from the
+ *     output and log-sum-exp).
+ *   - anthology-of-the-sota practice SOTA-114 (dmarx.github.io), "The general
+ *     form of the practice above it" (the fused chain matmul, scale, mask,
+ *     softmax, dropout, matmul) and "Cost" (each mask/dropout/head-dim/dtype
+ *     combination is its own code path; a silent fallback is a hazard).
+ *   - anthology-of-the-sota practice SOTA-085, "What 'when hardware supports
+ *     it' is carrying" (the result is exact; O(N) extra memory).
+ *
+ * Conventions shared by every entry point
+ *   Layout.  Q, K, V, O, dO, dQ, dK, dV are dense row-major (B, H, N, d)
+ *            arrays: element (b, h, i, c) sits at ((b*H + h)*N + i)*d + c.
+ *            lse and the backward's D are (B, H, N) float32.
+ *   Masks.   causal: key j is visible to query i iff j <= i (square N x N).
+ *            key padding: kv_len is a device array of B int32; key j is
+ *            visible iff j < kv_len[b] (values are clamped to [0, N]; query
+ *            rows at or past kv_len[b] are still computed). Both may be set.
+ *            A query row with no visible key yields O = 0, lse = -inf and
+ *            zero gradients.
+ *   Dropout. p in [0, 1). Each probability is kept iff the 32-bit draw
+ *            u = Philox4x32-10(counter = (j >> 2, i, h, b), key = seed)[j & 3]
+ *            satisfies u >= floor(p_f32 * 2^32); kept values are scaled by
+ *            1 / (1 - p). The log-sum-exp is over the undropped scores.
+ *            (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3".)
+ *   Memory.  All tensor pointers are device pointers owned by the caller and
+ *            must be 16-byte aligned. Outputs must not alias inputs. The
+ *            library never allocates, frees or synchronises; it keeps no
+ *            global state, so calls from several host threads are safe.
+ *   Streams. `stream` is a hipStream_t (NULL = the default stream). Work is
+ *            enqueued asynchronously; faults inside a kernel surface at the
+ *            caller's next synchronisation.
+ *   Errors.  Every argument is validated on the host before anything is
+ *            enqueued. An unsupported combination (head dimension, dtype)
+ *            returns ATTN_ERR_UNSUPPORTED: there is never a fallback path.
+ *            ATTN_ERR_LAUNCH reports a launch failure from the HIP runtime.
+ */
+#ifndef EXACT_TILED_ATTN_H
+#define EXACT_TILED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_F16 = 0,   /* IEEE binary16 */
+  ATTN_BF16 = 1,  /* bfloat16 */
+  ATTN_F32 = 2    /* IEEE binary32 (outputs only) */
+} attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,  /* NULL/misaligned pointer, bad size, bad p ... */
+  ATTN_ERR_UNSUPPORTED = 2,  /* valid request with no kernel (e.g. d = 96)  */
+  ATTN_ERR_WORKSPACE = 3,    /* backward workspace missing or too small     */
+  ATTN_ERR_LAUNCH = 4        /* the HIP runtime rejected a kernel launch    */
+} attn_status;
+
+typedef struct {
+  int32_t B, H, N, d;      /* batch, heads, sequence length, head dim.
+                              B, H, N >= 1; d in {64, 128};
+                              B*H*N*d must fit in int32 index math per head
+                              and the total element count below 2^62.      */
+  int32_t dtype;           /* attn_dtype of Q, K, V, dO: ATTN_F16 or BF16  */
+  int32_t out_dtype;       /* attn_dtype of O, dQ, dK, dV: == dtype or F32 */
+  float scale;             /* multiplies Q K^T; finite and nonzero         */
+  int32_t causal;          /* 0 or 1                                       */
+  const int32_t* kv_len;   /* device int32[B] of valid key counts, or NULL */
+  float dropout_p;         /* 0 <= p < 1; 0 disables dropout               */
+  uint64_t seed;           /* Philox key for dropout                       */
+} attn_params;
+
+/* Forward: O (out_dtype, (B,H,N,d)) and lse (float32, (B,H,N)), where
+ * lse_i = log sum_j exp(scale * Q_i . K_j) over the visible keys. */
+attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
+                     const void* v, void* o, float* lse, void* stream);
+
+/* Size in bytes of the workspace attn_bwd needs for these parameters
+ * (0 if the parameters are invalid). */
+size_t attn_bwd_workspace_bytes(const attn_params* p);
+
+/* Backward: given Q, K, V, the forward's O (out_dtype) and lse, and dO
+ * (dtype), writes dQ, dK, dV (out_dtype). Scores and probabilities are
+ * recomputed from lse; nothing N x N is stored. `workspace` is a device
+ * buffer of at least attn_bwd_workspace_bytes(p) bytes, owned by the caller,
+ * 256-byte aligned; its contents on entry do not matter. */
+attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
+                     const void* v, const void* o, const float* lse,
+                     const void* d_o, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Test aid: writes the dropout keep-mask keep[b][h][i][j] (uint8 0/1, device,
+ * (B,H,N,N)) that attn_fwd and attn_bwd use for these parameters. Masking by
+ * causal/kv_len is not applied here: it is the raw Philox keep decision. */
+attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* attn_status_string(attn_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_TILED_ATTN_H */

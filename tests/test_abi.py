@@ -1,0 +1,173 @@
+"""C-ABI tests that need no GPU: the library loads, exports every entry point
+declared in include/attn.h, and rejects every invalid argument on the host
+before anything is enqueued (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_20_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.LIB_PATH):
+        from exact_tiled_attention_20_amd import build
+        build.build(verbose=False)
+    return attn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(attn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.attn_version() == 100
+    for code, name in attn.STATUS_NAMES.items():
+        assert attn.status_string(code).startswith(name)
+    assert "unknown" in attn.status_string(99)
+
+
+def test_struct_layout_matches_header():
+    # int32 x 6, float, int32, pointer (8-aligned), float, uint64
+    assert ctypes.sizeof(attn.AttnParams) == 56
+    assert attn.AttnParams.kv_len.offset == 32
+    assert attn.AttnParams.seed.offset == 48
+
+
+FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation fails first
+SIZE = 1 << 40   # distinct ranges so no aliasing is reported
+
+
+def _ptrs(n):
+    return [FAKE + i * SIZE for i in range(n)]
+
+
+def _params(**kw):
+    base = dict(B=2, H=3, N=100, d=64, dtype=attn.ATTN_F16, out_dtype=attn.ATTN_F16,
+                scale=0.125, causal=False, dropout_p=0.0, seed=1)
+    raw_causal = kw.pop("causal", None)
+    base.update(kw)
+    B, H, N, d = base.pop("B"), base.pop("H"), base.pop("N"), base.pop("d")
+    p = attn.make_params(B, H, N, d, **base)
+    if raw_causal is not None:
+        p.causal = raw_causal
+    return p
+
+
+INVALID = [
+    dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(B=-1),
+    dict(dtype=7), dict(out_dtype=-1), dict(causal=2),
+    dict(scale=0.0), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(dropout_p=1.0), dict(dropout_p=-0.1), dict(dropout_p=float("nan")),
+    dict(N=1 << 24, d=128),           # N*d per head overflows int32 indexing
+    dict(B=1 << 16, H=1 << 15),       # B*H overflows
+]
+UNSUPPORTED = [
+    dict(d=96), dict(d=256), dict(d=32),
+    dict(dtype=attn.ATTN_F32, out_dtype=attn.ATTN_F32),
+    dict(dtype=attn.ATTN_F16, out_dtype=attn.ATTN_BF16),
+]
+
+
+def _fwd(lib, p, ptrs=None, stream=None):
+    q, k, v, o, lse = ptrs or _ptrs(5)
+    return lib.attn_fwd(ctypes.byref(p), q, k, v, o, lse, stream)
+
+
+def _bwd(lib, p, ptrs=None, ws_bytes=1 << 30):
+    q, k, v, o, lse, do, dq, dk, dv, ws = ptrs or _ptrs(10)
+    return lib.attn_bwd(ctypes.byref(p), q, k, v, o, lse, do, dq, dk, dv, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", INVALID)
+def test_invalid_params_rejected(lib, kw):
+    p = _params(**kw)
+    assert _fwd(lib, p) == 1
+    assert _bwd(lib, p) == 1
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p)) == 0
+    assert lib.attn_dropout_mask(ctypes.byref(p), FAKE, None) == 1
+
+
+@pytest.mark.parametrize("kw", UNSUPPORTED)
+def test_unsupported_combinations_never_fall_back(lib, kw):
+    p = _params(**kw)
+    assert _fwd(lib, p) == 2
+    assert _bwd(lib, p) == 2
+
+
+def test_null_params_pointer(lib):
+    assert lib.attn_fwd(None, *_ptrs(5), None) == 1
+    assert lib.attn_bwd_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("slot", range(5))
+def test_fwd_null_or_misaligned_pointer(lib, slot):
+    for bad in (0, FAKE + 8 + slot * SIZE):
+        ptrs = _ptrs(5)
+        ptrs[slot] = bad
+        assert _fwd(lib, _params(), ptrs) == 1
+
+
+@pytest.mark.parametrize("slot", range(9))
+def test_bwd_null_or_misaligned_pointer(lib, slot):
+    for bad in (0, FAKE + 4 + slot * SIZE):
+        ptrs = _ptrs(10)
+        ptrs[slot] = bad
+        assert _bwd(lib, _params(), ptrs) == 1
+
+
+def test_fwd_rejects_aliasing(lib):
+    q, k, v, o, lse = _ptrs(5)
+    assert _fwd(lib, _params(), [q, k, v, q, lse]) == 1          # o aliases q
+    assert _fwd(lib, _params(), [q, k, v, o, o + 1024]) == 1     # lse inside o
+
+
+def test_bwd_workspace_checks(lib):
+    p = _params()
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(p))
+    assert need == ((2 * 3 * 100 * 4 + 255) // 256) * 256
+    ptrs = _ptrs(10)
+    assert _bwd(lib, p, ptrs, ws_bytes=need - 1) == 3
+    bad = list(ptrs)
+    bad[9] = 0
+    assert _bwd(lib, p, bad, ws_bytes=need) == 3
+    bad[9] = FAKE + 9 * SIZE + 128           # not 256-byte aligned
+    assert _bwd(lib, p, bad, ws_bytes=need) == 3
+
+
+def test_bwd_rejects_output_aliasing(lib):
+    ptrs = _ptrs(10)
+    ptrs[7] = ptrs[6]                        # dk aliases dq
+    assert _bwd(lib, _params(), ptrs) == 1
+    ptrs = _ptrs(10)
+    ptrs[8] = ptrs[0]                        # dv aliases q
+    assert _bwd(lib, _params(), ptrs) == 1
+
+
+def test_misaligned_kv_len(lib):
+    p = _params()
+    p.kv_len = ctypes.c_void_p(FAKE + 2)
+    assert _fwd(lib, p) == 1
+
+
+def test_dropout_mask_pointer_checks(lib):
+    p = _params(dropout_p=0.1)
+    assert lib.attn_dropout_mask(ctypes.byref(p), None, None) == 1
+    assert lib.attn_dropout_mask(ctypes.byref(p), FAKE + 1, None) == 1
