@@ -1,0 +1,260 @@
+#!/usr/bin/env python
+"""Benchmark of the fused exact-attention path on one MI355X.
+
+One step = one pass of the whole path over one batch: attn_fwd (the fused tiled
+forward, O and lse) followed by the three backward kernels (D = rowsum(dO*O),
+dK/dV with recomputation, dQ with recomputation), on the 16K-token causal bf16
+workload B=1, H=32, N=16384, d=128 with dO ~ N(0,1). Inputs are resident on the
+device before timing starts; outputs and the workspace are preallocated.
+
+FLOP convention: forward 4*B*H*N^2*d, halved under the causal mask; backward
+2.5x forward (five N^2*d contractions against two). Throughput is reported in
+TFLOP/s and as a fraction of MI355X's dense bf16 MFMA peak (2516.6 TFLOP/s).
+
+Prints ONE JSON line. Options:
+  --gpus N      only 1 is supported (the path runs on one GPU)
+  --steps K     timed steps (default 10)
+  --warmup W    untimed steps first (default 3)
+  --no-cpu-baseline   skip timing the CPU oracle on its bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused attention TFLOP/s + % of fp16/bf16 MFMA peak, fwd and fwd+bwd"
+PEAK_BF16_TFLOPS = 2516.6          # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "ctx16k_b1h32n16384d128_bf16_causal_bwd"
+FWD_WORKLOAD = "long_b4h16n4096d128_bf16_causal"
+KERNEL_NAMES = ("attn_fwd_kernel", "attn_bwd_preprocess_kernel", "attn_bwd_dkdv_kernel",
+                "attn_bwd_dq_kernel")
+
+
+def _csrc_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_tiled_attention_20_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(f"{kernel}@{workload}")
+    if not rec or rec.get("csrc_digest") != _csrc_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, n_prefix: int = 16384, n_heads: int = 2) -> dict:
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
+    the first n_heads heads of batch 0, over the causal prefix of the first
+    n_prefix tokens (the whole sequence by default), forward and backward.
+    Rows of a causal prefix see only keys inside it, so the forward of the
+    sample is exactly part of the full computation."""
+    import numpy as np
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    n = min(n_prefix, w.N)
+    nh = min(n_heads, w.H)
+    sl = (slice(0, 1), slice(0, nh), slice(0, n))
+    q, k, v = inputs.q[sl], inputs.k[sl], inputs.v[sl]
+    do = inputs.do[sl] if inputs.do is not None else None
+    t0 = time.perf_counter()
+    A.forward(q, k, v, scale=w.scale, causal=w.causal)
+    passes = 1.0
+    if do is not None:
+        A.backward(q, k, v, do, scale=w.scale, causal=w.causal)
+        passes = 3.5
+    dt = time.perf_counter() - t0
+    flops = 4.0 * nh * n * n * w.d * (0.5 if w.causal else 1.0) * passes
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"batch 0, heads 0..{nh - 1}, first {n} tokens of the {w.name} inputs, "
+                      f"fp64 numpy {'fwd+bwd' if do is not None else 'fwd'} "
+                      f"({dt:.1f} s, {flops / 1e9:.0f} GFLOP)",
+            "seconds": round(dt, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time only the forward headline workload (for profiling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) "
+              "is not supported. Heads are independent, so a multi-GPU run would shard "
+              "(b, h) across GPUs with no communication; run one process per GPU instead.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import attn_workloads as W
+    import exact_tiled_attention_20_amd as attn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    attn.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # -- forward headline workload (4 x 16 heads, N = 4096, d = 128, causal) --
+    wf = W.WORKLOADS[FWD_WORKLOAD]
+    fi = W.make_inputs(wf)
+    fq, fk, fv = (t.to(dev) for t in (fi.q, fi.k, fi.v))
+    fo = torch.empty_like(fq)
+    flse = torch.empty(fq.shape[:3], dtype=torch.float32, device=dev)
+
+    def fwd_long():
+        attn.fwd(fq, fk, fv, causal=wf.causal, scale=wf.scale, out=fo, lse=flse)
+
+    for _ in range(max(args.warmup, 1)):
+        fwd_long()
+    torch.cuda.synchronize()
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fwd_long()
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_long_ms = e0.elapsed_time(e1) / reps
+    fwd_long_tflops = wf.flops_fwd() / (fwd_long_ms * 1e-3) / 1e12
+    del fq, fk, fv, fo, flse
+    if args.fwd_only:
+        print(json.dumps({"workload": FWD_WORKLOAD, "fwd_ms": fwd_long_ms,
+                          "fwd_tflops": fwd_long_tflops}))
+        return 0
+
+    # -- the step workload: forward + backward at B=1, H=32, N=16384, d=128 --
+    w = W.WORKLOADS[WORKLOAD]
+    inputs = W.make_inputs(w)
+    q, k, v, do = (t.to(dev) for t in (inputs.q, inputs.k, inputs.v, inputs.do))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(attn.bwd_workspace_bytes(q, causal=w.causal, scale=w.scale),
+                     dtype=torch.uint8, device=dev)
+    kw = dict(causal=w.causal, scale=w.scale)
+    stages = (attn.BWD_STAGE_PREPROCESS, attn.BWD_STAGE_DKDV, attn.BWD_STAGE_DQ)
+
+    def step(events=None):
+        if events is not None:
+            events[0].record()
+        attn.fwd(q, k, v, out=o, lse=lse, **kw)
+        for i, s in enumerate(stages):
+            if events is not None:
+                events[i + 1].record()
+            attn.bwd(q, k, v, o, lse, do, out=grads, workspace=ws, stage=s, **kw)
+        if events is not None:
+            events[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel = [0.0] * 4
+    step_ms = 0.0
+    for ev in evs:
+        for j in range(4):
+            per_kernel[j] += ev[j].elapsed_time(ev[j + 1]) / K
+        step_ms += ev[0].elapsed_time(ev[4]) / K
+    ms_per_step = wall * 1e3 / K
+
+    f_fwd = w.flops_fwd()
+    f_total = f_fwd + w.flops_bwd()
+    value = f_total / (ms_per_step * 1e-3) / 1e12
+    # Algorithmic FLOP per launch: the forward's two contractions; the dK/dV
+    # kernel's four (S, dP, dV, dK); the dQ kernel's one (dQ) -- its second
+    # evaluation of S and dP is recomputation beyond the algorithm's count.
+    alg = {"attn_fwd_kernel": f_fwd, "attn_bwd_preprocess_kernel": 0.0,
+           "attn_bwd_dkdv_kernel": 2.0 * f_fwd, "attn_bwd_dq_kernel": 0.5 * f_fwd}
+    kernels = {}
+    for name, ms in zip(KERNEL_NAMES, per_kernel):
+        kernels[name] = {"avg_ms": round(ms, 4),
+                         "alg_tflops": round(alg[name] / (ms * 1e-3) / 1e12, 2) if alg[name] else None}
+    # The preprocess kernel is HBM-bound: it reads dO and O, writes D.
+    pre_bytes = 2 * q.numel() * 2 + lse.numel() * 4
+    kernels["attn_bwd_preprocess_kernel"]["gbs"] = round(pre_bytes / (per_kernel[1] * 1e-3) / 1e9, 1)
+    dom = max(range(4), key=lambda j: per_kernel[j])
+    dom_name = KERNEL_NAMES[dom]
+    if alg[dom_name] > 0:
+        achieved = alg[dom_name] / (per_kernel[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = pre_bytes / (per_kernel[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = _traffic_for(dom_name, WORKLOAD)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "pass": "fwd+bwd"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"tflops": round(f_fwd / (per_kernel[0] * 1e-3) / 1e12, 2),
+                "pct_of_peak": round(100 * f_fwd / (per_kernel[0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "ms": round(per_kernel[0], 4)},
+        "fwd_long": {"workload": FWD_WORKLOAD, "ms": round(fwd_long_ms, 4),
+                     "tflops": round(fwd_long_tflops, 2),
+                     "pct_of_peak": round(100 * fwd_long_tflops / PEAK_BF16_TFLOPS, 2)},
+        "kernels": kernels,
+        "event_ms_per_step": round(step_ms, 4),
+        "roofline": roof,
+        "csrc_digest": _csrc_digest(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inputs)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

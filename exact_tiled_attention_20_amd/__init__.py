@@ -29,8 +29,9 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTE
                 3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_LAUNCH"}
 
 # Entry points declared in include/attn.h (checked by the ABI tests).
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_dropout_mask",
-           "attn_status_string", "attn_version")
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
+           "attn_dropout_mask", "attn_status_string", "attn_version")
+BWD_STAGE_PREPROCESS, BWD_STAGE_DKDV, BWD_STAGE_DQ = 0, 1, 2
 
 
 class AttnParams(ctypes.Structure):
@@ -72,6 +73,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_stage.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
+    lib.attn_bwd_stage.restype = ctypes.c_int
     lib.attn_bwd_workspace_bytes.argtypes = [P]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_dropout_mask.argtypes = [P, vp, vp]
@@ -183,8 +187,12 @@ def bwd_workspace_bytes(q, *, causal=False, kv_len=None, dropout_p=0.0, seed=0,
 
 def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None, dropout_p: float = 0.0,
         seed: int = 0, scale: Optional[float] = None, out_dtype=None,
-        workspace=None):
-    """Fused backward with recomputation: returns (dQ, dK, dV) in out_dtype."""
+        workspace=None, out=None, stage: Optional[int] = None):
+    """Fused backward with recomputation: returns (dQ, dK, dV) in out_dtype.
+
+    out: optional preallocated (dq, dk, dv); workspace: optional uint8 device
+    buffer of at least bwd_workspace_bytes(...) bytes; stage: None runs all
+    three kernels, else one of BWD_STAGE_* (see attn_bwd_stage)."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
@@ -199,15 +207,22 @@ def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None, dropout_p: fl
     need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty(q.shape, dtype=odt, device=q.device)
-    dk = torch.empty(q.shape, dtype=odt, device=q.device)
-    dv = torch.empty(q.shape, dtype=odt, device=q.device)
-    st = lib.attn_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                      lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                      dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                      _stream_ptr(q.device))
+    if out is None:
+        out = tuple(torch.empty(q.shape, dtype=odt, device=q.device) for _ in range(3))
+    dq, dk, dv = out
+    for t in out:
+        if t.dtype != odt or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError("gradient outputs must be contiguous, shaped like q, in out_dtype")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_ptr(q.device))
+    if stage is None:
+        st = lib.attn_bwd(ctypes.byref(p), *args)
+    else:
+        st = lib.attn_bwd_stage(ctypes.byref(p), int(stage), *args)
     if st != 0:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd" if stage is None else "attn_bwd_stage")
     return dq, dk, dv
 
 

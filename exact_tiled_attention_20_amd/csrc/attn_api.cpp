@@ -138,9 +138,11 @@ size_t attn_bwd_workspace_bytes(const attn_params* p) {
   return (stat_bytes(p) + 255) & ~size_t(255);
 }
 
-attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
-                     const void* o, const float* lse, const void* d_o, void* dq, void* dk,
-                     void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, const void* k,
+                            const void* v, const void* o, const float* lse, const void* d_o,
+                            void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (stage < -1 || stage > 2) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
   const void* ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
@@ -192,9 +194,23 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
   a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
   a.seed_hi = (uint32_t)(p->seed >> 32);
   const hipError_t e = attn::launch_bwd(p->dtype == ATTN_BF16 ? 1 : 0, p->d, p->causal != 0,
-                                        dropout, p->out_dtype == ATTN_F32, a,
+                                        dropout, p->out_dtype == ATTN_F32, stage, a,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                     void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, -1, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_bwd_stage(const attn_params* p, int32_t stage, const void* q, const void* k,
+                           const void* v, const void* o, const float* lse, const void* d_o,
+                           void* dq, void* dk, void* dv, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (stage < ATTN_BWD_STAGE_PREPROCESS || stage > ATTN_BWD_STAGE_DQ) return ATTN_ERR_INVALID_ARG;
+  return bwd_impl(p, stage, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream) {

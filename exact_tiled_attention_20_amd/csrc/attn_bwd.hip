@@ -506,49 +506,57 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
 }
 
 template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
-static hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
-  const long long rows = (long long)a.B * a.H * a.N;
-  const long long threads = rows * (D / 8);
-  hipLaunchKernelGGL((attn_bwd_preprocess_kernel<E, D, OUT_F32>),
-                     dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nkb = (a.N + 127) / 128;
-  const int tk = a.B * a.H * nkb;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>),
-                     dim3(((tk + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nqb = (a.N + 127) / 128;
-  const int tq = a.B * a.H * nqb;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>),
-                     dim3(((tq + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
-  return hipGetLastError();
+static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (stage < 0 || stage == 0) {
+    const long long rows = (long long)a.B * a.H * a.N;
+    const long long threads = rows * (D / 8);
+    hipLaunchKernelGGL((attn_bwd_preprocess_kernel<E, D, OUT_F32>),
+                       dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage < 0 || stage == 1) {
+    const int nkb = (a.N + 127) / 128;
+    const int tk = a.B * a.H * nkb;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>),
+                       dim3(((tk + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage < 0 || stage == 2) {
+    const int nqb = (a.N + 127) / 128;
+    const int tq = a.B * a.H * nqb;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>),
+                       dim3(((tq + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <typename E, int D>
-static hipError_t launch_d(bool causal, bool dropout, bool out_f32, const BwdArgs& a,
+static hipError_t launch_d(bool causal, bool dropout, bool out_f32, int st, const BwdArgs& a,
                            hipStream_t s) {
   if (causal) {
-    if (dropout) return out_f32 ? launch_all<E, D, true, true, true>(a, s)
-                                : launch_all<E, D, true, true, false>(a, s);
-    return out_f32 ? launch_all<E, D, true, false, true>(a, s)
-                   : launch_all<E, D, true, false, false>(a, s);
+    if (dropout) return out_f32 ? launch_all<E, D, true, true, true>(st, a, s)
+                                : launch_all<E, D, true, true, false>(st, a, s);
+    return out_f32 ? launch_all<E, D, true, false, true>(st, a, s)
+                   : launch_all<E, D, true, false, false>(st, a, s);
   }
-  if (dropout) return out_f32 ? launch_all<E, D, false, true, true>(a, s)
-                              : launch_all<E, D, false, true, false>(a, s);
-  return out_f32 ? launch_all<E, D, false, false, true>(a, s)
-                 : launch_all<E, D, false, false, false>(a, s);
+  if (dropout) return out_f32 ? launch_all<E, D, false, true, true>(st, a, s)
+                              : launch_all<E, D, false, true, false>(st, a, s);
+  return out_f32 ? launch_all<E, D, false, false, true>(st, a, s)
+                 : launch_all<E, D, false, false, false>(st, a, s);
 }
 
-hipError_t launch_bwd(int dtype, int d, bool causal, bool dropout, bool out_f32,
+hipError_t launch_bwd(int dtype, int d, bool causal, bool dropout, bool out_f32, int stage,
                       const BwdArgs& a, hipStream_t stream) {
   if (dtype == 1) {
-    if (d == 128) return launch_d<Elem<bf16_t>, 128>(causal, dropout, out_f32, a, stream);
-    return launch_d<Elem<bf16_t>, 64>(causal, dropout, out_f32, a, stream);
+    if (d == 128) return launch_d<Elem<bf16_t>, 128>(causal, dropout, out_f32, stage, a, stream);
+    return launch_d<Elem<bf16_t>, 64>(causal, dropout, out_f32, stage, a, stream);
   }
-  if (d == 128) return launch_d<Elem<f16_t>, 128>(causal, dropout, out_f32, a, stream);
-  return launch_d<Elem<f16_t>, 64>(causal, dropout, out_f32, a, stream);
+  if (d == 128) return launch_d<Elem<f16_t>, 128>(causal, dropout, out_f32, stage, a, stream);
+  return launch_d<Elem<f16_t>, 64>(causal, dropout, out_f32, stage, a, stream);
 }
 
 }  // namespace attn

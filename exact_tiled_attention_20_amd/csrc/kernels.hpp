@@ -71,7 +71,8 @@ struct MaskArgs {
 // outputs. Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(int dtype, int d, bool causal, bool dropout, bool out_f32,
                       const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd(int dtype, int d, bool causal, bool dropout, bool out_f32,
+// stage: -1 = all three kernels, else 0 (preprocess), 1 (dK/dV), 2 (dQ).
+hipError_t launch_bwd(int dtype, int d, bool causal, bool dropout, bool out_f32, int stage,
                       const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dropout_mask(const MaskArgs& a, hipStream_t stream);
 

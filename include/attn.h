@@ -110,6 +110,26 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
                      const void* d_o, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The three steps attn_bwd enqueues, callable one at a time (same arguments
+ * and validation as attn_bwd; each ignores the outputs it does not write).
+ * Calling them in this order on one stream equals attn_bwd:
+ *   ATTN_BWD_STAGE_PREPROCESS  D_i = dO_i . O_i into the workspace
+ *   ATTN_BWD_STAGE_DKDV        dK, dV (reads the workspace)
+ *   ATTN_BWD_STAGE_DQ          dQ     (reads the workspace)
+ * Useful for timing each kernel with events, or for overlapping dQ with
+ * other work on a second stream once the preprocess step has run. */
+typedef enum {
+  ATTN_BWD_STAGE_PREPROCESS = 0,
+  ATTN_BWD_STAGE_DKDV = 1,
+  ATTN_BWD_STAGE_DQ = 2
+} attn_bwd_stage_id;
+
+attn_status attn_bwd_stage(const attn_params* p, int32_t stage, const void* q,
+                           const void* k, const void* v, const void* o,
+                           const float* lse, const void* d_o, void* dq, void* dk,
+                           void* dv, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Test aid: writes the dropout keep-mask keep[b][h][i][j] (uint8 0/1, device,
  * (B,H,N,N)) that attn_fwd and attn_bwd use for these parameters. Masking by
  * causal/kv_len is not applied here: it is the raw Philox keep decision. */

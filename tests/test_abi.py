@@ -152,6 +152,17 @@ def test_bwd_workspace_checks(lib):
     assert _bwd(lib, p, bad, ws_bytes=need) == 3
 
 
+def test_bwd_stage_validation(lib):
+    q, k, v, o, lse, do, dq, dk, dv, ws = _ptrs(10)
+    p = _params()
+    for bad_stage in (-1, 3, 100):
+        assert lib.attn_bwd_stage(ctypes.byref(p), bad_stage, q, k, v, o, lse, do, dq, dk, dv,
+                                  ws, 1 << 30, None) == 1
+    p = _params(d=96)
+    assert lib.attn_bwd_stage(ctypes.byref(p), 1, q, k, v, o, lse, do, dq, dk, dv,
+                              ws, 1 << 30, None) == 2
+
+
 def test_bwd_rejects_output_aliasing(lib):
     ptrs = _ptrs(10)
     ptrs[7] = ptrs[6]                        # dk aliases dq
