@@ -43,7 +43,7 @@ attn_status check_params(const attn_params* p) {
   if (p->out_dtype != ATTN_F16 && p->out_dtype != ATTN_BF16 && p->out_dtype != ATTN_F32)
     return ATTN_ERR_INVALID_ARG;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARG;
-  if (!std::isfinite(p->scale) || p->scale == 0.0f) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(p->scale) || !(p->scale > 0.0f)) return ATTN_ERR_INVALID_ARG;
   if (!(p->dropout_p >= 0.0f && p->dropout_p < 1.0f)) return ATTN_ERR_INVALID_ARG;
   // Element counts: per head N*d must index in 32 bits; the whole tensor must
   // stay far from overflow of 64-bit byte offsets; the grids must fit.
@@ -121,6 +121,7 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   a.per_xcd = (a.total + 7) / 8;
   a.scale = p->scale;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  a.rescale_thr = 8.0f / a.scale_log2;
   const bool dropout = p->dropout_p > 0.0f;
   a.drop_threshold = drop_threshold(p->dropout_p);
   a.drop_rescale = 1.0f / (1.0f - p->dropout_p);

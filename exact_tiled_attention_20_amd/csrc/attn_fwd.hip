@@ -122,14 +122,39 @@ void attn_fwd_kernel(const FwdArgs a) {
     }
   };
 
+  // Loop-invariant LDS offsets. The swizzle depends only on the low four row
+  // bits, so moving by 32 K rows or 16 V rows is a plain byte offset.
+  int koff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = lds_off<D>(l32, (kk * 2 + hh) * 16);
+  const int g = lane >> 4;
+  const int i16 = lane & 15;
+  int voff[2][NDB];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      voff[half][db] = lds_off<D>(4 * hh + (i16 >> 2) + 8 * half,
+                                  (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2);
+
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m = -INFINITY;   // running max of raw scores (scale * q.k)
-  float l = 0.f;         // this half-lane's share of the running denominator
+  // m_ref: reference maximum (raw q.k units) that the exponentials are taken
+  // against. It is raised only when a tile's row maximum exceeds it by more
+  // than 2^8 in probability, so the O rescale runs rarely; O and l always
+  // share the same reference, which keeps O / l exact.
+  float m_ref = -INFINITY;
+  // This half-lane's share of the running denominator, twice: l sums the fp32
+  // probabilities (it defines lse); lr sums the same probabilities rounded to
+  // the MFMA operand type (it normalises O, so a row dominated by one key
+  // reproduces that key's value row without a normalisation gap).
+  float l = 0.f;
+  float lr = 0.f;
   const float c2 = a.scale_log2;
+  const float thr = a.rescale_thr;
 
   if (ntiles > 0) {
     load_tile(0);
@@ -152,12 +177,12 @@ void attn_fwd_kernel(const FwdArgs a) {
       for (int kb2 = 0; kb2 < NKB; ++kb2) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb2][r] = 0.f;
-        const int row = kb2 * 32 + l32;
+        u32x4 af[KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 af = *(const u32x4*)(kb + lds_off<D>(row, (kk * 2 + hh) * 16));
-          s[kb2] = E::mfma(af, qf[kk], s[kb2]);
-        }
+        for (int kk = 0; kk < KK; ++kk)
+          af[kk] = *(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk]);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s[kb2] = E::mfma(af[kk], qf[kk], s[kb2]);
       }
       // Mask: causal diagonal tiles, the ragged tail and key padding.
       const bool need_mask = (CAUSAL && (k0 + BC - 1 > wq0)) || (k0 + BC > kv_end);
@@ -177,11 +202,19 @@ void attn_fwd_kernel(const FwdArgs a) {
       for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
-      mx = fmaxf(mx, wave_swap_halves(mx));
-      const float m_new = fmaxf(m, mx);
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m - m_ref) * c2);
-      const float mb = m_ref * c2;
+      mx = halves_max(mx);
+      const bool raise = mx > m_ref + thr;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * c2) : 1.f;
+        if (raise) m_ref = mx;
+        l *= alpha;
+        lr *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      }
+      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
       float rs = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2)
@@ -191,64 +224,64 @@ void attn_fwd_kernel(const FwdArgs a) {
           rs += p;
           s[kb2][r] = p;
         }
-      l = __builtin_fmaf(l, alpha, rs);
-      m = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      if (DROPOUT) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int j0 = k0 + kb2 * 32 + 8 * g + 4 * hh;
-            const u32x4 u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h,
-                                          (uint32_t)b, a.seed_lo, a.seed_hi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (u[e] < a.drop_threshold) s[kb2][4 * g + e] = 0.f;
-          }
-      }
+      l += rs;
       // P^T as MFMA B operands: 16 keys per step, 8 per lane.
       u32x4 pf[NC16];
+      float rr_sum = 0.f;
 #pragma unroll
       for (int c = 0; c < NC16; ++c) {
         const int kb2 = c >> 1;
         const int rr = (c & 1) * 8;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pf[c][e] = E::pack2(s[kb2][rr + 2 * e], s[kb2][rr + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) {
+          pf[c][e] = E::pack2(s[kb2][rr + 2 * e], s[kb2][rr + 2 * e + 1]);
+          rr_sum = E::add_pair(pf[c][e], rr_sum);
+        }
+      }
+      lr += rr_sum;
+      if (DROPOUT) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int j0 = k0 + kb2 * 32 + 8 * g4 + 4 * hh;
+            const u32x4 u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h,
+                                          (uint32_t)b, a.seed_lo, a.seed_hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (u[e] < a.drop_threshold) s[kb2][4 * g4 + e] = 0.f;
+          }
+#pragma unroll
+        for (int c = 0; c < NC16; ++c) {
+          const int kb2 = c >> 1;
+          const int rr = (c & 1) * 8;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pf[c][e] = E::pack2(s[kb2][rr + 2 * e], s[kb2][rr + 2 * e + 1]);
+        }
       }
       // O^T += V^T P^T. Lane (group g = lane/16, i = lane%16) addresses row
       // 16c + 4hh + i/4 (+8) and columns 32db + 16(g&1) + 4(i&3) .. +4.
-      const int g = lane >> 4;
-      const int i16 = lane & 15;
 #pragma unroll
       for (int c = 0; c < NC16; ++c) {
-        const int row1 = c * 16 + 4 * hh + (i16 >> 2);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int byte = (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2;
-          const i16x4 lo = lds_read_tr16(vb, lds_off<D>(row1, byte));
-          const i16x4 hi = lds_read_tr16(vb, lds_off<D>(row1 + 8, byte));
-          u32x4 af;
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-          const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-          af[0] = lo2[0];
-          af[1] = lo2[1];
-          af[2] = hi2[0];
-          af[3] = hi2[1];
-          acc[db] = E::mfma(af, pf[c], acc[db]);
+          const u32x2 lo = __builtin_bit_cast(
+              u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[0][db]));
+          const u32x2 hi = __builtin_bit_cast(
+              u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[1][db]));
+          acc[db] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[c], acc[db]);
         }
       }
     }
     if (more) store_tile(buf ^ 1);
   }
 
-  // Epilogue: O = O_acc / l (times 1/(1-p) under dropout), lse = m + ln l.
-  const float lt = l + wave_swap_halves(l);
+  // Epilogue: O = O_acc / lr (times 1/(1-p) under dropout), lse = m + ln l.
+  const float lt = halves_sum(l);
+  const float lrt = halves_sum(lr);
   if (qi < N) {
-    float inv = (lt > 0.f) ? (1.f / lt) : 0.f;
+    float inv = (lrt > 0.f) ? (1.f / lrt) : 0.f;
     if (DROPOUT) inv *= a.drop_rescale;
     const size_t orow = head + (size_t)qi * D;
 #pragma unroll
@@ -269,7 +302,7 @@ void attn_fwd_kernel(const FwdArgs a) {
         }
       }
     if (hh == 0) {
-      a.lse[(size_t)bh * N + qi] = (lt > 0.f) ? (a.scale * m + logf(lt)) : -INFINITY;
+      a.lse[(size_t)bh * N + qi] = (lt > 0.f) ? (a.scale * m_ref + logf(lt)) : -INFINITY;
     }
   }
 }

@@ -25,6 +25,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Storage element tags. Both are 16-bit in memory.
@@ -39,14 +42,18 @@ template <> struct Elem<bf16_t> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  // Round-to-nearest-even pack of two floats into one dword (lo, hi).
+  // Round-to-nearest-even pack of two floats into one dword (lo, hi):
+  // a single v_cvt_pk_bf16_f32.
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
   }
   static __device__ __forceinline__ float to_float(uint16_t x) {
     return __uint_as_float((uint32_t)x << 16);
+  }
+  // acc + lo + hi of a packed pair (v_dot2c_f32_bf16 against (1, 1)).
+  static __device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
   }
 };
 template <> struct Elem<f16_t> {
@@ -56,13 +63,17 @@ template <> struct Elem<f16_t> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+  // v_cvt_pk_f16_f32 (round to nearest even).
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
   }
   static __device__ __forceinline__ float to_float(uint16_t x) {
     return (float)__builtin_bit_cast(_Float16, x);
+  }
+  // acc + lo + hi of a packed pair (v_dot2c_f32_f16 against (1, 1)).
+  static __device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
   }
 };
 
@@ -134,6 +145,21 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_base, int byte_of
 __device__ __forceinline__ float wave_swap_halves(float x) {
   // Exchange with the lane 32 positions away (lanes 0..31 <-> 32..63).
   return __shfl_xor(x, 32, 64);
+}
+
+// max / sum of x over lanes l and l^32 with one v_permlane32_swap: the swap
+// returns (x of the upper half in the lower lanes, x of the lower half in the
+// upper lanes) beside the untouched copies, so combining the pair gives the
+// two-lane result in every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 }  // namespace attn

@@ -31,6 +31,8 @@ struct FwdArgs {
   int total;             // B * H * nqb
   float scale;           // softmax scale (fp32)
   float scale_log2;      // scale * log2(e)
+  float rescale_thr;     // raise the reference max when a row max exceeds it
+                         // by this much (raw q.k units): 8 / scale_log2
   uint32_t drop_threshold;  // keep iff draw >= threshold
   float drop_rescale;       // 1 / (1 - p)
   uint32_t seed_lo, seed_hi;

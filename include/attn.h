@@ -84,7 +84,7 @@ typedef struct {
                               and the total element count below 2^62.      */
   int32_t dtype;           /* attn_dtype of Q, K, V, dO: ATTN_F16 or BF16  */
   int32_t out_dtype;       /* attn_dtype of O, dQ, dK, dV: == dtype or F32 */
-  float scale;             /* multiplies Q K^T; finite and nonzero         */
+  float scale;             /* multiplies Q K^T; finite and > 0             */
   int32_t causal;          /* 0 or 1                                       */
   const int32_t* kv_len;   /* device int32[B] of valid key counts, or NULL */
   float dropout_p;         /* 0 <= p < 1; 0 disables dropout               */

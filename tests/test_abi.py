@@ -74,7 +74,7 @@ def _params(**kw):
 INVALID = [
     dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(B=-1),
     dict(dtype=7), dict(out_dtype=-1), dict(causal=2),
-    dict(scale=0.0), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(scale=0.0), dict(scale=-0.125), dict(scale=float("inf")), dict(scale=float("nan")),
     dict(dropout_p=1.0), dict(dropout_p=-0.1), dict(dropout_p=float("nan")),
     dict(N=1 << 24, d=128),           # N*d per head overflows int32 indexing
     dict(B=1 << 16, H=1 << 15),       # B*H overflows
