@@ -14,9 +14,10 @@
 // Mapping to CDNA4:
 //   * One workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32
 //     query rows. Q stays in VGPRs as MFMA B operands for the whole pass.
-//   * K and V tiles of 64 keys are staged HBM -> VGPR -> LDS, double-buffered,
-//     one barrier per tile, in a chunk-swizzled row-major layout. K is read by
-//     rows; V is read with ds_read_b64_tr_b16, so no transpose is stored.
+//   * K and V tiles of 64 keys are copied HBM -> LDS directly
+//     (global_load_lds_dwordx4), double-buffered, one barrier per tile, in a
+//     chunk-swizzled row-major layout. K is read by rows; V is read with
+//     ds_read_b64_tr_b16, so no transpose is stored.
 //   * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16): each
 //     lane then owns one query row, so the running max, the denominator and the
 //     O rescale factor are per-lane scalars; the row maximum needs a single
@@ -66,7 +67,7 @@ void attn_fwd_kernel(const FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -92,33 +93,34 @@ void attn_fwd_kernel(const FwdArgs a) {
   char* const kb0 = smem;
   char* const vb0 = smem + 2 * TILE_BYTES;
 
-  u32x4 kr[CPT], vr[CPT];
-  auto load_tile = [&](int t) {
+  // K/V tiles are copied HBM -> LDS directly. Each wave fills SPW slices of
+  // 1 KiB per tile; within a slice lane l fills LDS chunk l, which holds the
+  // logical chunk (l % CPR) ^ swizzle(row) of tile row slice*RPS + l / CPR.
+  constexpr int RPS = 1024 / (D * 2);       // rows per 1 KiB slice: 4 or 8
+  constexpr int SPW = TILE_BYTES / 1024 / 4;  // slices per wave per tile: 4 or 2
+  uint32_t goff[SPW];   // byte offset of this lane's source chunk within a tile
+  int grow[SPW];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int id = tid + kFwdThreads * u;
-      const int row = id / CPR;
-      const int c = id - row * CPR;
-      const int key = t * BC + row;
-      if (key < kv_end) {
-        kr[u] = *(const u32x4*)(K + (size_t)key * D + c * 8);
-        vr[u] = *(const u32x4*)(V + (size_t)key * D + c * 8);
-      } else {
-        kr[u] = u32x4{0, 0, 0, 0};
-        vr[u] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* kb = kb0 + buf * TILE_BYTES;
-    char* vb = vb0 + buf * TILE_BYTES;
+  for (int u = 0; u < SPW; ++u) {
+    const int slice = w * SPW + u;
+    grow[u] = slice * RPS + lane / CPR;
+    goff[u] = (uint32_t)(grow[u] * D * 2 + (((lane % CPR) ^ lds_swz<D>(grow[u])) << 4));
+  }
+  auto issue_tile = [&](int t, int buf) {
+    const int key0 = t * BC;
+    const char* kt = (const char*)K + (size_t)key0 * D * 2;   // wave-uniform bases
+    const char* vt = (const char*)V + (size_t)key0 * D * 2;
+    const bool partial = key0 + BC > kv_end;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int id = tid + kFwdThreads * u;
-      const int row = id / CPR;
-      const int c = id - row * CPR;
-      *(u32x4*)(kb + lds_off<D>(row, c * 16)) = kr[u];
-      *(u32x4*)(vb + lds_off<D>(row, c * 16)) = vr[u];
+    for (int u = 0; u < SPW; ++u) {
+      uint32_t off = goff[u];
+      // Rows past the valid keys repeat the last valid row: finite data that
+      // the mask then excludes (its probability is exactly zero).
+      if (partial && key0 + grow[u] >= kv_end)
+        off += (uint32_t)((kv_end - 1 - key0 - grow[u]) * D * 2);
+      const int dst = buf * TILE_BYTES + (w * SPW + u) * 1024;
+      load_lds16(kt + off, kb0 + dst);
+      load_lds16(vt + off, vb0 + dst);
     }
   };
 
@@ -156,16 +158,16 @@ void attn_fwd_kernel(const FwdArgs a) {
   const float c2 = a.scale_log2;
   const float thr = a.rescale_thr;
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) issue_tile(0, 0);
 
   for (int t = 0; t < ntiles; ++t) {
+    // Tile t has landed in LDS once every wave's copies are complete.
+    wait_all_memory();
     __syncthreads();
     const int buf = t & 1;
     const bool more = (t + 1) < ntiles;
-    if (more) load_tile(t + 1);
+    // Buffer buf^1 was last read in iteration t-1, which every wave has left.
+    if (more) issue_tile(t + 1, buf ^ 1);
     const int k0 = t * BC;
     const bool active = wave_has_rows && (!CAUSAL || k0 <= wq0 + 31);
     if (active) {
@@ -274,7 +276,6 @@ void attn_fwd_kernel(const FwdArgs a) {
         }
       }
     }
-    if (more) store_tile(buf ^ 1);
   }
 
   // Epilogue: O = O_acc / lr (times 1/(1-p) under dropout), lse = m + ln l.

@@ -126,16 +126,29 @@ __device__ __forceinline__ u32x4 dropout_draws(uint32_t t, uint32_t i, uint32_t 
 // bits rotate the 64-byte segment with row%4 and whose two low bits take the
 // next row bits, so both patterns touch every bank once per 256 bytes.
 template <int D>
+__device__ __forceinline__ int lds_swz(int row) {
+  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+template <int D>
 __device__ __forceinline__ int lds_off(int row, int byte_in_row) {
   constexpr int CPR = D / 8;  // 16-byte chunks per row: 16 (D=128) or 8 (D=64)
-  int sw;
-  if (D == 128)
-    sw = ((row & 3) << 2) | ((row >> 2) & 3);
-  else
-    sw = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  const int chunk = (byte_in_row >> 4) ^ sw;
+  const int chunk = (byte_in_row >> 4) ^ lds_swz<D>(row);
   return row * (D * 2) + ((chunk & (CPR - 1)) << 4) + (byte_in_row & 15);
 }
+
+// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l
+// writes LDS bytes [lds_base + 16 l, +16). lds_base must be wave-uniform.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// Wait until every outstanding memory operation of this wave has completed,
+// including HBM -> LDS copies (which count as vector-memory loads).
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_base, int byte_off) {
   const char* p = (const char*)lds_base + byte_off;
