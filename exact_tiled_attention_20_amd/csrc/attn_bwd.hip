@@ -61,21 +61,20 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs 
 
 // ---------------------------------------------------------------------------
 // dK, dV. Workgroup: 128 keys of one (b, h); wave w owns keys kw .. kw+31.
+// Q and dO tiles of 64 query rows (and their lse and D values) are copied
+// HBM -> LDS directly and processed as two 32-row halves.
 template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int BKW = 128;             // keys per workgroup
-  constexpr int BQ = kBwdBlockQ;       // queries per LDS tile (2 sub-blocks of 32)
+  constexpr int BQ = kBwdBlockQ;       // queries per LDS tile (2 halves of 32)
   constexpr int KK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TILE_BYTES = BQ * D * 2;
-  constexpr int CPR = D / 8;
-  constexpr int CPT = BQ * CPR / kBwdThreads;
-  static_assert(CPT >= 1, "tile too small");
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
-  __shared__ __attribute__((aligned(16))) float s_del[2][BQ];
+  __shared__ __attribute__((aligned(256))) float s_lse[2][BQ];
+  __shared__ __attribute__((aligned(256))) float s_del[2][BQ];
 
   const int nkb = (a.N + BKW - 1) / BKW;
   const int total = a.B * a.H * nkb;
@@ -97,7 +96,7 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int k0 = kblk * BKW;
@@ -130,70 +129,41 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
       }
     }
     const bool wave_has_keys = kw < kv_end;
+    const bool key_tail = kw + 32 > kv_end;
     const int qt0 = CAUSAL ? (k0 / BQ) : 0;
     const int nqt = (N + BQ - 1) / BQ;
     char* const qb0 = smem;
     char* const ob0 = smem + 2 * TILE_BYTES;
-
-    u32x4 qr[CPT], orr[CPT];
-    float lse_r = 0.f, del_r = 0.f;
-    auto load_tile = [&](int t) {
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) {
-        const int id = tid + kBwdThreads * u;
-        const int row = id / CPR;
-        const int c = id - row * CPR;
-        const int qi = t * BQ + row;
-        if (qi < N) {
-          qr[u] = *(const u32x4*)(Q + (size_t)qi * D + c * 8);
-          orr[u] = *(const u32x4*)(dO + (size_t)qi * D + c * 8);
-        } else {
-          qr[u] = u32x4{0, 0, 0, 0};
-          orr[u] = u32x4{0, 0, 0, 0};
-        }
-      }
-      if (tid < BQ) {
-        const int qi = t * BQ + tid;
-        // Rows past N or with no visible key contribute nothing: P = 0.
-        float ls = INFINITY, dl = 0.f;
-        if (qi < N) {
-          const float x = LSE[qi];
-          ls = (x == -INFINITY) ? INFINITY : x * kLog2e;
-          dl = DEL[qi];
-        }
-        lse_r = ls;
-        del_r = dl;
-      }
-    };
-    auto store_tile = [&](int buf) {
-      char* qb = qb0 + buf * TILE_BYTES;
-      char* ob = ob0 + buf * TILE_BYTES;
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) {
-        const int id = tid + kBwdThreads * u;
-        const int row = id / CPR;
-        const int c = id - row * CPR;
-        *(u32x4*)(qb + lds_off<D>(row, c * 16)) = qr[u];
-        *(u32x4*)(ob + lds_off<D>(row, c * 16)) = orr[u];
-      }
-      if (tid < BQ) {
-        s_lse[buf][tid] = lse_r;
-        s_del[buf][tid] = del_r;
-      }
+    TilePairLoader<D, BQ, 4> loader;
+    loader.init(w, lane);
+    // lse and D of the tile's rows: one dword per lane, waves 0 and 1.
+    auto issue_tile = [&](int t, int buf) {
+      loader.issue(Q, dO, t * BQ, N, qb0 + buf * TILE_BYTES, ob0 + buf * TILE_BYTES);
+      const int row = min(t * BQ + lane, N - 1);
+      if (w == 0) load_lds4(LSE + row, &s_lse[buf][0]);
+      if (w == 1) load_lds4(DEL + row, &s_del[buf][0]);
     };
 
-    const float c2 = a.scale_log2;
-    if (qt0 < nqt) {
-      load_tile(qt0);
-      store_tile(0);
-    }
+    int roff[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) roff[kk] = lds_off<D>(l32, (kk * 2 + hh) * 16);
     const int g = lane >> 4;
     const int i16 = lane & 15;
+    int toff[2][NDB];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        toff[half][db] = lds_off<D>(4 * hh + (i16 >> 2) + 8 * half,
+                                    (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2);
+
+    const float c2 = a.scale_log2;
+    if (qt0 < nqt) issue_tile(qt0, 0);
     for (int t = qt0; t < nqt; ++t) {
+      wait_all_memory();
       __syncthreads();
       const int buf = (t - qt0) & 1;
-      const bool more = (t + 1) < nqt;
-      if (more) load_tile(t + 1);
+      if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
       const char* qb = qb0 + buf * TILE_BYTES;
       const char* ob = ob0 + buf * TILE_BYTES;
 #pragma unroll
@@ -201,6 +171,7 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
         const int qbase = t * BQ + 32 * sub;
         const bool active = wave_has_keys && qbase < N && (!CAUSAL || qbase + 31 >= kw);
         if (!active) continue;
+        const bool need_mask = (CAUSAL && qbase < kw + 31) || key_tail || (qbase + 32 > N);
         // S = Q K^T and dP = dO V^T (32 queries x 32 keys), lane = key.
         f32x16 s, dp;
 #pragma unroll
@@ -208,17 +179,13 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
           s[r] = 0.f;
           dp[r] = 0.f;
         }
-        const int row = 32 * sub + l32;
+        const int rbase = sub * 32 * D * 2;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 qa = *(const u32x4*)(qb + lds_off<D>(row, (kk * 2 + hh) * 16));
-          s = E::mfma(qa, kf[kk], s);
-        }
+        for (int kk = 0; kk < KK; ++kk)
+          s = E::mfma(*(const u32x4*)(qb + rbase + roff[kk]), kf[kk], s);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 oa = *(const u32x4*)(ob + lds_off<D>(row, (kk * 2 + hh) * 16));
-          dp = E::mfma(oa, vf[kk], dp);
-        }
+        for (int kk = 0; kk < KK; ++kk)
+          dp = E::mfma(*(const u32x4*)(ob + rbase + roff[kk]), vf[kk], dp);
         // P, dropout, dS. Register r holds query qbase + 8(r/4) + 4hh + r%4.
         f32x16 pz, ds;
 #pragma unroll
@@ -230,9 +197,11 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
             const int qi = qbase + 8 * g4 + 4 * hh + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[e]));
-            const bool dead = (CAUSAL && j > qi) || (j >= kv_end);
-            if (dead) p = 0.f;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[e] * kLog2e));
+            if (need_mask) {
+              const bool dead = (CAUSAL && j > qi) || (j >= kv_end) || (qi >= N);
+              if (dead) p = 0.f;
+            }
             float z = 1.f;
             if (DROPOUT) {
               const u32x4 u = dropout_draws((uint32_t)j >> 2, (uint32_t)qi, (uint32_t)h,
@@ -252,27 +221,18 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
             pa[e] = E::pack2(pz[8 * c + 2 * e], pz[8 * c + 2 * e + 1]);
             sa[e] = E::pack2(ds[8 * c + 2 * e], ds[8 * c + 2 * e + 1]);
           }
-          const int row1 = 32 * sub + 16 * c + 4 * hh + (i16 >> 2);
+          const int tbase = (32 * sub + 16 * c) * D * 2;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const int byte = (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2;
-            u32x4 ob4, qb4;
-            {
-              const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(ob, lds_off<D>(row1, byte)));
-              const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(ob, lds_off<D>(row1 + 8, byte)));
-              ob4 = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            }
-            {
-              const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(qb, lds_off<D>(row1, byte)));
-              const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(qb, lds_off<D>(row1 + 8, byte)));
-              qb4 = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            }
-            dv[db] = E::mfma(pa, ob4, dv[db]);
-            dk[db] = E::mfma(sa, qb4, dk[db]);
+            const u32x2 olo = __builtin_bit_cast(u32x2, lds_read_tr16(ob, tbase + toff[0][db]));
+            const u32x2 ohi = __builtin_bit_cast(u32x2, lds_read_tr16(ob, tbase + toff[1][db]));
+            const u32x2 qlo = __builtin_bit_cast(u32x2, lds_read_tr16(qb, tbase + toff[0][db]));
+            const u32x2 qhi = __builtin_bit_cast(u32x2, lds_read_tr16(qb, tbase + toff[1][db]));
+            dv[db] = E::mfma(pa, u32x4{olo[0], olo[1], ohi[0], ohi[1]}, dv[db]);
+            dk[db] = E::mfma(sa, u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dk[db]);
           }
         }
       }
-      if (more) store_tile(buf ^ 1);
     }
   }
 
@@ -299,19 +259,20 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ. Workgroup: 128 queries of one (b, h); wave w owns 32 query rows.
+// dQ. Workgroup: 128 queries of one (b, h); wave w owns 32 query rows. The
+// forward's orientation: S^T = K Q^T and dP^T = V dO^T put one query per lane,
+// so lse_i and D_i are per-lane scalars, and the packed dS^T registers are the
+// B operand of dQ^T += K^T dS^T (K read transposed from LDS). K/V tiles of 64
+// keys are copied HBM -> LDS directly; each tile is processed as two 32-key
+// halves to keep two waves per SIMD.
 template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(const BwdArgs a) {
   constexpr int BR = 128;
   constexpr int BC = 64;
   constexpr int KK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int NKB = BC / 32;
-  constexpr int NC16 = BC / 16;
   constexpr int TILE_BYTES = BC * D * 2;
-  constexpr int CPR = D / 8;
-  constexpr int CPT = BC * CPR / kBwdThreads;
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
 
@@ -335,7 +296,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -369,35 +330,21 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
 
   char* const kb0 = smem;
   char* const vb0 = smem + 2 * TILE_BYTES;
-  u32x4 kr[CPT], vr[CPT];
-  auto load_tile = [&](int t) {
+  TilePairLoader<D, BC, 4> loader;
+  loader.init(w, lane);
+
+  int roff[KK];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int id = tid + kBwdThreads * u;
-      const int row = id / CPR;
-      const int c = id - row * CPR;
-      const int key = t * BC + row;
-      if (key < kv_end) {
-        kr[u] = *(const u32x4*)(K + (size_t)key * D + c * 8);
-        vr[u] = *(const u32x4*)(V + (size_t)key * D + c * 8);
-      } else {
-        kr[u] = u32x4{0, 0, 0, 0};
-        vr[u] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* kb = kb0 + buf * TILE_BYTES;
-    char* vb = vb0 + buf * TILE_BYTES;
+  for (int kk = 0; kk < KK; ++kk) roff[kk] = lds_off<D>(l32, (kk * 2 + hh) * 16);
+  const int g = lane >> 4;
+  const int i16 = lane & 15;
+  int toff[2][NDB];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int id = tid + kBwdThreads * u;
-      const int row = id / CPR;
-      const int c = id - row * CPR;
-      *(u32x4*)(kb + lds_off<D>(row, c * 16)) = kr[u];
-      *(u32x4*)(vb + lds_off<D>(row, c * 16)) = vr[u];
-    }
-  };
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      toff[half][db] = lds_off<D>(4 * hh + (i16 >> 2) + 8 * half,
+                                  (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2);
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -405,84 +352,73 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   const float c2 = a.scale_log2;
-  const int g = lane >> 4;
-  const int i16 = lane & 15;
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) loader.issue(K, V, 0, kv_end, kb0, vb0);
   for (int t = 0; t < ntiles; ++t) {
+    wait_all_memory();
     __syncthreads();
     const int buf = t & 1;
-    const bool more = (t + 1) < ntiles;
-    if (more) load_tile(t + 1);
+    if (t + 1 < ntiles)
+      loader.issue(K, V, (t + 1) * BC, kv_end, kb0 + (buf ^ 1) * TILE_BYTES,
+                   vb0 + (buf ^ 1) * TILE_BYTES);
     const int k0 = t * BC;
     const bool active = wave_has_rows && (!CAUSAL || k0 <= wq0 + 31);
-    if (active) {
-      const char* kb = kb0 + buf * TILE_BYTES;
-      const char* vb = vb0 + buf * TILE_BYTES;
-      f32x16 s[NKB], dp[NKB];
+    if (!active) continue;
+    const char* kb = kb0 + buf * TILE_BYTES;
+    const char* vb = vb0 + buf * TILE_BYTES;
+    const bool need_mask = (CAUSAL && (k0 + BC - 1 > wq0)) || (k0 + BC > kv_end);
 #pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2) {
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      // S^T and dP^T for keys k0 + 32 kb2 .. +32 (lane = query).
+      f32x16 s, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[kb2][r] = 0.f;
-          dp[kb2][r] = 0.f;
-        }
-        const int row = kb2 * 32 + l32;
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+      const int rbase = kb2 * 32 * D * 2;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 ka = *(const u32x4*)(kb + lds_off<D>(row, (kk * 2 + hh) * 16));
-          s[kb2] = E::mfma(ka, qf[kk], s[kb2]);
-        }
+      for (int kk = 0; kk < KK; ++kk)
+        s = E::mfma(*(const u32x4*)(kb + rbase + roff[kk]), qf[kk], s);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 va = *(const u32x4*)(vb + lds_off<D>(row, (kk * 2 + hh) * 16));
-          dp[kb2] = E::mfma(va, of[kk], dp[kb2]);
+      for (int kk = 0; kk < KK; ++kk)
+        dp = E::mfma(*(const u32x4*)(vb + rbase + roff[kk]), of[kk], dp);
+      // dS^T = P^T (Z dP^T - D); register r is key k0 + 32kb2 + 8(r/4) + 4hh + r%4.
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int j0 = k0 + kb2 * 32 + 8 * g4 + 4 * hh;
+        u32x4 u = u32x4{0, 0, 0, 0};
+        if (DROPOUT)
+          u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h, (uint32_t)b,
+                            a.seed_lo, a.seed_hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
+          if (need_mask) {
+            const int jj = j0 + e;
+            if ((CAUSAL && jj > qi) || jj >= kv_end) p = 0.f;
+          }
+          float dpz = dp[r];
+          if (DROPOUT) dpz = (u[e] >= a.drop_threshold) ? dpz * a.drop_rescale : 0.f;
+          s[r] = p * (dpz - dlt);
         }
       }
-      // dS^T = P^T (Z dP^T - D); register r of block kb2 is key
-      // k0 + 32kb2 + 8(r/4) + 4hh + r%4 of this lane's query row.
+      // dQ^T += K^T dS^T, two 16-key MFMA steps.
 #pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int j0 = k0 + kb2 * 32 + 8 * g4 + 4 * hh;
-          u32x4 u = u32x4{0, 0, 0, 0};
-          if (DROPOUT)
-            u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h, (uint32_t)b,
-                              a.seed_lo, a.seed_hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            const int jj = j0 + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c2, -lse2));
-            if ((CAUSAL && jj > qi) || jj >= kv_end) p = 0.f;
-            float z = 1.f;
-            if (DROPOUT) z = (u[e] >= a.drop_threshold) ? a.drop_rescale : 0.f;
-            s[kb2][r] = p * (dp[kb2][r] * z - dlt);
-          }
-        }
-      // dQ^T += K^T dS^T, 16 keys per MFMA step; K read transposed from LDS.
-#pragma unroll
-      for (int c = 0; c < NC16; ++c) {
-        const int kb2 = c >> 1;
-        const int rr = (c & 1) * 8;
+      for (int c = 0; c < 2; ++c) {
         u32x4 sb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sb[e] = E::pack2(s[kb2][rr + 2 * e], s[kb2][rr + 2 * e + 1]);
-        const int row1 = c * 16 + 4 * hh + (i16 >> 2);
+        for (int e = 0; e < 4; ++e) sb[e] = E::pack2(s[8 * c + 2 * e], s[8 * c + 2 * e + 1]);
+        const int tbase = (kb2 * 2 + c) * 16 * D * 2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int byte = (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2;
-          const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(kb, lds_off<D>(row1, byte)));
-          const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(kb, lds_off<D>(row1 + 8, byte)));
+          const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(kb, tbase + toff[0][db]));
+          const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(kb, tbase + toff[1][db]));
           acc[db] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sb, acc[db]);
         }
       }
     }
-    if (more) store_tile(buf ^ 1);
   }
 
   if (qi < N) {

@@ -44,9 +44,6 @@ void attn_fwd_kernel(const FwdArgs a) {
   constexpr int NKB = BC / 32;          // 32-key blocks of S^T per tile
   constexpr int NC16 = BC / 16;         // 16-key MFMA steps of the PV product
   constexpr int TILE_BYTES = BC * D * 2;
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int CPT = BC * CPR / kFwdThreads;  // chunks per thread per tile
-  static_assert(CPT >= 1, "tile too small for the workgroup");
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
 
@@ -93,35 +90,11 @@ void attn_fwd_kernel(const FwdArgs a) {
   char* const kb0 = smem;
   char* const vb0 = smem + 2 * TILE_BYTES;
 
-  // K/V tiles are copied HBM -> LDS directly. Each wave fills SPW slices of
-  // 1 KiB per tile; within a slice lane l fills LDS chunk l, which holds the
-  // logical chunk (l % CPR) ^ swizzle(row) of tile row slice*RPS + l / CPR.
-  constexpr int RPS = 1024 / (D * 2);       // rows per 1 KiB slice: 4 or 8
-  constexpr int SPW = TILE_BYTES / 1024 / 4;  // slices per wave per tile: 4 or 2
-  uint32_t goff[SPW];   // byte offset of this lane's source chunk within a tile
-  int grow[SPW];
-#pragma unroll
-  for (int u = 0; u < SPW; ++u) {
-    const int slice = w * SPW + u;
-    grow[u] = slice * RPS + lane / CPR;
-    goff[u] = (uint32_t)(grow[u] * D * 2 + (((lane % CPR) ^ lds_swz<D>(grow[u])) << 4));
-  }
+  // K/V tiles are copied HBM -> LDS directly, in the swizzled layout.
+  TilePairLoader<D, BC, 4> loader;
+  loader.init(w, lane);
   auto issue_tile = [&](int t, int buf) {
-    const int key0 = t * BC;
-    const char* kt = (const char*)K + (size_t)key0 * D * 2;   // wave-uniform bases
-    const char* vt = (const char*)V + (size_t)key0 * D * 2;
-    const bool partial = key0 + BC > kv_end;
-#pragma unroll
-    for (int u = 0; u < SPW; ++u) {
-      uint32_t off = goff[u];
-      // Rows past the valid keys repeat the last valid row: finite data that
-      // the mask then excludes (its probability is exactly zero).
-      if (partial && key0 + grow[u] >= kv_end)
-        off += (uint32_t)((kv_end - 1 - key0 - grow[u]) * D * 2);
-      const int dst = buf * TILE_BYTES + (w * SPW + u) * 1024;
-      load_lds16(kt + off, kb0 + dst);
-      load_lds16(vt + off, vb0 + dst);
-    }
+    loader.issue(K, V, t * BC, kv_end, kb0 + buf * TILE_BYTES, vb0 + buf * TILE_BYTES);
   };
 
   // Loop-invariant LDS offsets. The swizzle depends only on the low four row

@@ -146,6 +146,53 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
+// Copies ROWS x D tiles of two row-major (rows, D) arrays A and B from HBM into
+// LDS in the lds_off layout, NWAVES waves sharing the work: each wave fills
+// SPW slices of 1 KiB per tile; within a slice lane l fills LDS chunk l, which
+// holds logical chunk (l % CPR) ^ swizzle(row) of tile row slice*RPS + l/CPR.
+// Rows at or past `valid` repeat row valid-1 (finite data the caller masks).
+template <int D, int ROWS, int NWAVES>
+struct TilePairLoader {
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE_BYTES = ROWS * D * 2;
+  static constexpr int RPS = 1024 / (D * 2);
+  static constexpr int SPW = TILE_BYTES / 1024 / NWAVES;
+  static_assert(SPW >= 1 && SPW * NWAVES * 1024 == TILE_BYTES, "tile does not split evenly");
+  uint32_t goff[SPW];
+  int grow[SPW];
+  int wave;
+
+  __device__ __forceinline__ void init(int w, int lane) {
+    wave = w;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      grow[u] = (w * SPW + u) * RPS + lane / CPR;
+      goff[u] = (uint32_t)(grow[u] * D * 2 + (((lane % CPR) ^ lds_swz<D>(grow[u])) << 4));
+    }
+  }
+  // Tile rows [row0, row0 + ROWS) of A and B into lds_a / lds_b.
+  __device__ __forceinline__ void issue(const uint16_t* A, const uint16_t* B, int row0,
+                                        int valid, char* lds_a, char* lds_b) const {
+    const char* at = (const char*)A + (size_t)row0 * D * 2;
+    const char* bt = (const char*)B + (size_t)row0 * D * 2;
+    const bool partial = row0 + ROWS > valid;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      uint32_t off = goff[u];
+      if (partial && row0 + grow[u] >= valid)
+        off += (uint32_t)((valid - 1 - row0 - grow[u]) * D * 2);
+      const int dst = (wave * SPW + u) * 1024;
+      load_lds16(at + off, lds_a + dst);
+      load_lds16(bt + off, lds_b + dst);
+    }
+  }
+};
+
+// 4-byte variant: lane l writes LDS bytes [lds_base + 4 l, +4).
+__device__ __forceinline__ void load_lds4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_base, 4, 0, 0);
+}
+
 // Wait until every outstanding memory operation of this wave has completed,
 // including HBM -> LDS copies (which count as vector-memory loads).
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
