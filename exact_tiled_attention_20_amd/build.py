@@ -23,9 +23,12 @@ SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_dropout_mask.hi
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled: only scalar/vector fp32 ops are emitted.
+# MFMA results are placed in VGPRs rather than AGPRs, so the softmax arithmetic
+# that consumes score tiles needs no accumulator-register copies.
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -21,6 +21,8 @@
 //   3. dQ: one workgroup per 128 queries (4 waves x 32 queries), the forward's
 //      orientation (S^T = K Q^T, one query per lane) plus dP^T = V dO^T; dQ^T =
 //      K^T dS^T reads K transposed from LDS. Deterministic: no atomics.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -61,20 +63,30 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs 
 
 // ---------------------------------------------------------------------------
 // dK, dV. Workgroup: 128 keys of one (b, h); wave w owns keys kw .. kw+31.
-// Q and dO tiles of 64 query rows (and their lse and D values) are copied
-// HBM -> LDS directly and processed as two 32-row halves.
+// The workgroup's K and V rows stay in LDS for the whole pass; Q and dO tiles
+// of 64 query rows (with their lse and D values) stream HBM -> LDS directly,
+// double-buffered, and are processed as two 32-row halves in a software
+// pipeline: the S and dP products of the next half are issued before the VALU
+// work of the current half, so the matrix cores run while P and dS are formed.
 template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int BKW = 128;             // keys per workgroup
-  constexpr int BQ = kBwdBlockQ;       // queries per LDS tile (2 halves of 32)
+  constexpr int BQ = 64;               // query rows per LDS tile
+  constexpr int NSUB = BQ / 32;
   constexpr int KK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TILE_BYTES = BQ * D * 2;
+  constexpr int KV_BYTES = BKW * D * 2;
 
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
-  __shared__ __attribute__((aligned(256))) float s_lse[2][BQ];
-  __shared__ __attribute__((aligned(256))) float s_del[2][BQ];
+  __shared__ __attribute__((aligned(1024)))
+      char smem[2 * KV_BYTES + 4 * TILE_BYTES + 4 * BQ * sizeof(float)];
+  char* const ks0 = smem;                                  // K rows of the block
+  char* const vs0 = smem + KV_BYTES;                       // V rows of the block
+  char* const qb0 = smem + 2 * KV_BYTES;                   // [2] Q tiles
+  char* const ob0 = qb0 + 2 * TILE_BYTES;                  // [2] dO tiles
+  float* const s_lse = (float*)(ob0 + 2 * TILE_BYTES);     // [2][BQ]
+  float* const s_del = s_lse + 2 * BQ;                     // [2][BQ]
 
   const int nkb = (a.N + BKW - 1) / BKW;
   const int total = a.B * a.H * nkb;
@@ -116,37 +128,28 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     }
 
   if (k0 < kv_end) {
-    // K and V rows of this lane's key as B operands (K^T, V^T columns).
-    u32x4 kf[KK], vf[KK];
-    {
-      const int jr = min(j, N - 1);
-      const uint16_t* ks = K + (size_t)jr * D + hh * 8;
-      const uint16_t* vs = V + (size_t)jr * D + hh * 8;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        kf[kk] = *(const u32x4*)(ks + kk * 16);
-        vf[kk] = *(const u32x4*)(vs + kk * 16);
-      }
-    }
-    const bool wave_has_keys = kw < kv_end;
     const bool key_tail = kw + 32 > kv_end;
     const int qt0 = CAUSAL ? (k0 / BQ) : 0;
     const int nqt = (N + BQ - 1) / BQ;
-    char* const qb0 = smem;
-    char* const ob0 = smem + 2 * TILE_BYTES;
+    {
+      TilePairLoader<D, BKW, 4> kvload;
+      kvload.init(w, lane);
+      kvload.issue(K, V, k0, kv_end, ks0, vs0);
+    }
     TilePairLoader<D, BQ, 4> loader;
     loader.init(w, lane);
-    // lse and D of the tile's rows: one dword per lane, waves 0 and 1.
+    // lse (wave 0) and D (wave 1) of the tile's rows, one dword per lane.
     auto issue_tile = [&](int t, int buf) {
       loader.issue(Q, dO, t * BQ, N, qb0 + buf * TILE_BYTES, ob0 + buf * TILE_BYTES);
       const int row = min(t * BQ + lane, N - 1);
-      if (w == 0) load_lds4(LSE + row, &s_lse[buf][0]);
-      if (w == 1) load_lds4(DEL + row, &s_del[buf][0]);
+      if (w == 0) load_lds4(LSE + row, s_lse + buf * BQ);
+      if (w == 1) load_lds4(DEL + row, s_del + buf * BQ);
     };
 
-    int roff[KK];
+    int roff[KK];     // row-read offsets (A operands and the K/V B operands)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) roff[kk] = lds_off<D>(l32, (kk * 2 + hh) * 16);
+    const int kvrow = 32 * w * D * 2;   // this wave's 32 key rows inside ks0 / vs0
     const int g = lane >> 4;
     const int i16 = lane & 15;
     int toff[2][NDB];
@@ -156,8 +159,8 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
       for (int db = 0; db < NDB; ++db)
         toff[half][db] = lds_off<D>(4 * hh + (i16 >> 2) + 8 * half,
                                     (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2);
-
     const float c2 = a.scale_log2;
+
     if (qt0 < nqt) issue_tile(qt0, 0);
     for (int t = qt0; t < nqt; ++t) {
       wait_all_memory();
@@ -166,14 +169,11 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
       if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
       const char* qb = qb0 + buf * TILE_BYTES;
       const char* ob = ob0 + buf * TILE_BYTES;
-#pragma unroll
-      for (int sub = 0; sub < BQ / 32; ++sub) {
-        const int qbase = t * BQ + 32 * sub;
-        const bool active = wave_has_keys && qbase < N && (!CAUSAL || qbase + 31 >= kw);
-        if (!active) continue;
-        const bool need_mask = (CAUSAL && qbase < kw + 31) || key_tail || (qbase + 32 > N);
-        // S = Q K^T and dP = dO V^T (32 queries x 32 keys), lane = key.
-        f32x16 s, dp;
+      const float* lse_t = s_lse + buf * BQ;
+      const float* del_t = s_del + buf * BQ;
+
+      // S = Q K^T and dP = dO V^T for half `sub` (32 queries x 32 keys).
+      auto sdp = [&](int sub, f32x16& s, f32x16& dp) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           s[r] = 0.f;
@@ -182,25 +182,32 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
         const int rbase = sub * 32 * D * 2;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          s = E::mfma(*(const u32x4*)(qb + rbase + roff[kk]), kf[kk], s);
+          s = E::mfma(*(const u32x4*)(qb + rbase + roff[kk]),
+                      *(const u32x4*)(ks0 + kvrow + roff[kk]), s);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          dp = E::mfma(*(const u32x4*)(ob + rbase + roff[kk]), vf[kk], dp);
-        // P, dropout, dS. Register r holds query qbase + 8(r/4) + 4hh + r%4.
+          dp = E::mfma(*(const u32x4*)(ob + rbase + roff[kk]),
+                       *(const u32x4*)(vs0 + kvrow + roff[kk]), dp);
+      };
+      // P (masked), dropout, dS; packed as MFMA A operands for 16-query steps.
+      // Register r holds query qbase + 8(r/4) + 4hh + r%4.
+      auto grad = [&](int sub, const f32x16& s, const f32x16& dp, u32x4 (&pa)[2],
+                      u32x4 (&sa)[2], auto masked) {
+        const int qbase = t * BQ + 32 * sub;
         f32x16 pz, ds;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int ql = 32 * sub + 8 * g4 + 4 * hh;
-          const f32x4 ls4 = *(const f32x4*)&s_lse[buf][ql];
-          const f32x4 dl4 = *(const f32x4*)&s_del[buf][ql];
+          const f32x4 ls4 = *(const f32x4*)&lse_t[ql];
+          const f32x4 dl4 = *(const f32x4*)&del_t[ql];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
             const int qi = qbase + 8 * g4 + 4 * hh + e;
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[e] * kLog2e));
-            if (need_mask) {
-              const bool dead = (CAUSAL && j > qi) || (j >= kv_end) || (qi >= N);
-              if (dead) p = 0.f;
+            if (decltype(masked)::value) {
+              const bool dead = (CAUSAL & (j > qi)) | (j >= kv_end) | (qi >= N);
+              p = dead ? 0.f : p;
             }
             float z = 1.f;
             if (DROPOUT) {
@@ -212,15 +219,18 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
             ds[r] = p * (dp[r] * z - dl4[e]);
           }
         }
-        // dV += (P Z)^T dO and dK += dS^T Q; 16 queries per MFMA step.
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          u32x4 pa, sa;
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pa[e] = E::pack2(pz[8 * c + 2 * e], pz[8 * c + 2 * e + 1]);
-            sa[e] = E::pack2(ds[8 * c + 2 * e], ds[8 * c + 2 * e + 1]);
+            pa[c][e] = E::pack2(pz[8 * c + 2 * e], pz[8 * c + 2 * e + 1]);
+            sa[c][e] = E::pack2(ds[8 * c + 2 * e], ds[8 * c + 2 * e + 1]);
           }
+      };
+      // dV += (P Z)^T dO and dK += dS^T Q with dO, Q read transposed.
+      auto dvdk = [&](int sub, const u32x4 (&pa)[2], const u32x4 (&sa)[2]) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
           const int tbase = (32 * sub + 16 * c) * D * 2;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
@@ -228,9 +238,31 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
             const u32x2 ohi = __builtin_bit_cast(u32x2, lds_read_tr16(ob, tbase + toff[1][db]));
             const u32x2 qlo = __builtin_bit_cast(u32x2, lds_read_tr16(qb, tbase + toff[0][db]));
             const u32x2 qhi = __builtin_bit_cast(u32x2, lds_read_tr16(qb, tbase + toff[1][db]));
-            dv[db] = E::mfma(pa, u32x4{olo[0], olo[1], ohi[0], ohi[1]}, dv[db]);
-            dk[db] = E::mfma(sa, u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dk[db]);
+            dv[db] = E::mfma(pa[c], u32x4{olo[0], olo[1], ohi[0], ohi[1]}, dv[db]);
+            dk[db] = E::mfma(sa[c], u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dk[db]);
           }
+        }
+      };
+
+      f32x16 s_c, dp_c;
+      sdp(0, s_c, dp_c);
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        f32x16 s_n, dp_n;
+        if (sub + 1 < NSUB) sdp(sub + 1, s_n, dp_n);
+        __builtin_amdgcn_sched_barrier(0);
+        const int qbase = t * BQ + 32 * sub;
+        const bool need_mask = (CAUSAL && qbase < kw + 31) || key_tail || (qbase + 32 > N);
+        u32x4 pa[2], sa[2];
+        if (need_mask)
+          grad(sub, s_c, dp_c, pa, sa, std::true_type());
+        else
+          grad(sub, s_c, dp_c, pa, sa, std::false_type());
+        __builtin_amdgcn_sched_barrier(0);
+        dvdk(sub, pa, sa);
+        if (sub + 1 < NSUB) {
+          s_c = s_n;
+          dp_c = dp_n;
         }
       }
     }
