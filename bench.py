@@ -104,6 +104,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only the forward headline workload (for profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (reference for "
+                         "hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -123,6 +126,17 @@ def main() -> int:
     attn.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        # 1 GiB read + 1 GiB written per launch: the known traffic against
+        # which FETCH_SIZE / WRITE_SIZE counter readings are scaled.
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel() * 2, "launches": 3}))
+        return 0
 
     # -- forward headline workload (4 x 16 heads, N = 4096, d = 128, causal) --
     wf = W.WORKLOADS[FWD_WORKLOAD]
