@@ -148,10 +148,12 @@ def main() -> int:
     def fwd_long():
         attn.fwd(fq, fk, fv, causal=wf.causal, scale=wf.scale, out=fo, lse=flse)
 
-    for _ in range(max(args.warmup, 1)):
+    # One launch takes well under a millisecond, so the clocks need a few dozen
+    # launches to settle before the timed repetitions.
+    for _ in range(max(args.warmup, 1) * 20):
         fwd_long()
     torch.cuda.synchronize()
-    reps = 20
+    reps = 100
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):

@@ -244,11 +244,12 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
         }
       };
 
-      f32x16 s_c, dp_c;
-      sdp(0, s_c, dp_c);
-#pragma unroll
-      for (int sub = 0; sub < NSUB; ++sub) {
-        f32x16 s_n, dp_n;
+      // Two 32-row halves: the S/dP products of the second half are issued
+      // before the softmax-gradient arithmetic of the first.
+      static_assert(NSUB == 2, "the half pipeline below assumes 64-row tiles");
+      auto step = [&](auto sub_c, const f32x16& s_c, const f32x16& dp_c, f32x16& s_n,
+                      f32x16& dp_n) {
+        constexpr int sub = decltype(sub_c)::value;
         if (sub + 1 < NSUB) sdp(sub + 1, s_n, dp_n);
         __builtin_amdgcn_sched_barrier(0);
         const int qbase = t * BQ + 32 * sub;
@@ -260,11 +261,11 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
           grad(sub, s_c, dp_c, pa, sa, std::false_type());
         __builtin_amdgcn_sched_barrier(0);
         dvdk(sub, pa, sa);
-        if (sub + 1 < NSUB) {
-          s_c = s_n;
-          dp_c = dp_n;
-        }
-      }
+      };
+      f32x16 s0, dp0, s1, dp1;
+      sdp(0, s0, dp0);
+      step(std::integral_constant<int, 0>(), s0, dp0, s1, dp1);
+      step(std::integral_constant<int, 1>(), s1, dp1, s0, dp0);
     }
   }
 
