@@ -89,12 +89,10 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   float* const s_del = s_lse + 2 * BQ;                     // [2][BQ]
 
   const int nkb = (a.N + BKW - 1) / BKW;
-  const int total = a.B * a.H * nkb;
-  const int per_xcd = (total + 7) / 8;
-  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (item >= total) return;
-  const int bh = item / nkb;
-  const int kblk = item - bh * nkb;    // ascending: heaviest first under causal
+  const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, nkb);
+  if (!wi.valid) return;
+  const int bh = wi.bh;
+  const int kblk = wi.rank;            // ascending: heaviest first under causal
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int N = a.N;
@@ -310,13 +308,10 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
 
   const int nqb = (a.N + BR - 1) / BR;
-  const int total = a.B * a.H * nqb;
-  const int per_xcd = (total + 7) / 8;
-  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (item >= total) return;
-  const int bh = item / nqb;
-  int qblk = item - bh * nqb;
-  if (CAUSAL) qblk = nqb - 1 - qblk;
+  const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, nqb);
+  if (!wi.valid) return;
+  const int bh = wi.bh;
+  const int qblk = CAUSAL ? nqb - 1 - wi.rank : wi.rank;  // heaviest first
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int N = a.N;
@@ -391,9 +386,12 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
     wait_all_memory();
     __syncthreads();
     const int buf = t & 1;
-    if (t + 1 < ntiles)
-      loader.issue(K, V, (t + 1) * BC, kv_end, kb0 + (buf ^ 1) * TILE_BYTES,
-                   vb0 + (buf ^ 1) * TILE_BYTES);
+    // Untracked, so that no LDS read of tile t waits for this prefetch; the
+    // wait at the top of the next iteration orders it before its readers.
+    if (t + 1 < ntiles) {
+      loader.issue_one_untracked(K, (t + 1) * BC, kv_end, kb0 + (buf ^ 1) * TILE_BYTES);
+      loader.issue_one_untracked(V, (t + 1) * BC, kv_end, vb0 + (buf ^ 1) * TILE_BYTES);
+    }
     const int k0 = t * BC;
     const bool active = wave_has_rows && (!CAUSAL || k0 <= wq0 + 31);
     if (!active) continue;

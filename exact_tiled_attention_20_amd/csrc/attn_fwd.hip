@@ -27,8 +27,8 @@
 //     permuted consistently on the V side by the transpose reads).
 //   * Work items are dealt out so that all query blocks of one head run on the
 //     same XCD (workgroup ids are dispatched round-robin over the 8 XCDs), which
-//     keeps that head's K/V re-reads in one L2; causal heads start with their
-//     heaviest (last) query block.
+//     keeps that head's K/V re-reads in one L2; under a causal mask the
+//     heaviest (last) query blocks of all of an XCD's heads start first.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -47,12 +47,10 @@ void attn_fwd_kernel(const FwdArgs a) {
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
 
-  const int bid = blockIdx.x;
-  const int item = (bid & 7) * a.per_xcd + (bid >> 3);
-  if (item >= a.total) return;
-  const int bh = item / a.nqb;
-  int qb = item - bh * a.nqb;
-  if (CAUSAL) qb = a.nqb - 1 - qb;
+  const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, a.nqb);
+  if (!wi.valid) return;
+  const int bh = wi.bh;
+  const int qb = CAUSAL ? a.nqb - 1 - wi.rank : wi.rank;  // heaviest first
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int N = a.N;
@@ -93,8 +91,13 @@ void attn_fwd_kernel(const FwdArgs a) {
   // K/V tiles are copied HBM -> LDS directly, in the swizzled layout.
   TilePairLoader<D, BC, 4> loader;
   loader.init(w, lane);
+  // The copies are issued untracked: the compiler would otherwise make the
+  // first LDS read after them wait for their completion, which would serialise
+  // the prefetch of tile t+1 with the PV product of tile t. The wait at the
+  // top of each iteration orders them before every read of their buffer.
   auto issue_tile = [&](int t, int buf) {
-    loader.issue(K, V, t * BC, kv_end, kb0 + buf * TILE_BYTES, vb0 + buf * TILE_BYTES);
+    loader.issue_one_untracked(K, t * BC, kv_end, kb0 + buf * TILE_BYTES);
+    loader.issue_one_untracked(V, t * BC, kv_end, vb0 + buf * TILE_BYTES);
   };
 
   // Loop-invariant LDS offsets. The swizzle depends only on the low four row
@@ -147,18 +150,18 @@ void attn_fwd_kernel(const FwdArgs a) {
       const char* kb = kb0 + buf * TILE_BYTES;
       const char* vb = vb0 + buf * TILE_BYTES;
       // S^T = K Q^T, 32 keys x 32 queries per block.
+      // The NKB accumulator chains are interleaved step by step: a single
+      // chain of dependent MFMAs cannot issue at the full rate.
       f32x16 s[NKB];
 #pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2) {
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb2][r] = 0.f;
-        u32x4 af[KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          af[kk] = *(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk]);
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s[kb2] = E::mfma(af[kk], qf[kk], s[kb2]);
-      }
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+          s[kb2] = E::mfma(*(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk]), qf[kk], s[kb2]);
       // Mask: causal diagonal tiles, the ragged tail and key padding.
       const bool need_mask = (CAUSAL && (k0 + BC - 1 > wq0)) || (k0 + BC > kv_end);
       if (need_mask) {

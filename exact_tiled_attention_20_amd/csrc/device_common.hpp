@@ -151,6 +151,30 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
 // SPW slices of 1 KiB per tile; within a slice lane l fills LDS chunk l, which
 // holds logical chunk (l % CPR) ^ swizzle(row) of tile row slice*RPS + l/CPR.
 // Rows at or past `valid` repeat row valid-1 (finite data the caller masks).
+// The same 16-byte copy written as inline assembly: base is wave-uniform,
+// voff is this lane's byte offset, lds_base the wave-uniform destination.
+// Writing M0 needs one wait state before the copy reads it. The copy counts
+// against vmcnt like any vector load.
+__device__ __forceinline__ void load_lds16_untracked(const void* base, uint32_t voff,
+                                                     void* lds_base) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_t*)lds_base;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(m0v)
+      : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order); LDS and export counters are not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int D, int ROWS, int NWAVES>
 struct TilePairLoader {
   static constexpr int CPR = D / 8;
@@ -170,6 +194,39 @@ struct TilePairLoader {
       goff[u] = (uint32_t)(grow[u] * D * 2 + (((lane % CPR) ^ lds_swz<D>(grow[u])) << 4));
     }
   }
+  // Tile rows [row0, row0 + ROWS) of one array into lds, issued so that the
+  // compiler does not track the copy: no wait for it is inserted before later
+  // LDS reads, and the caller orders every read of the destination after
+  // wait_vm() and a barrier.
+  __device__ __forceinline__ void issue_one_untracked(const uint16_t* A, int row0, int valid,
+                                                      char* lds) const {
+    const char* at = (const char*)A + (size_t)row0 * D * 2;
+    if (row0 + ROWS <= valid) {  // full tile (wave-uniform branch)
+#pragma unroll
+      for (int u = 0; u < SPW; ++u)
+        load_lds16_untracked(at, goff[u], lds + (wave * SPW + u) * 1024);
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      uint32_t off = goff[u];
+      if (row0 + grow[u] >= valid) off += (uint32_t)((valid - 1 - row0 - grow[u]) * D * 2);
+      load_lds16_untracked(at, off, lds + (wave * SPW + u) * 1024);
+    }
+  }
+  // Tile rows [row0, row0 + ROWS) of one array into lds.
+  __device__ __forceinline__ void issue_one(const uint16_t* A, int row0, int valid,
+                                            char* lds) const {
+    const char* at = (const char*)A + (size_t)row0 * D * 2;
+    const bool partial = row0 + ROWS > valid;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      uint32_t off = goff[u];
+      if (partial && row0 + grow[u] >= valid)
+        off += (uint32_t)((valid - 1 - row0 - grow[u]) * D * 2);
+      load_lds16(at + off, lds + (wave * SPW + u) * 1024);
+    }
+  }
   // Tile rows [row0, row0 + ROWS) of A and B into lds_a / lds_b.
   __device__ __forceinline__ void issue(const uint16_t* A, const uint16_t* B, int row0,
                                         int valid, char* lds_a, char* lds_b) const {
@@ -187,6 +244,36 @@ struct TilePairLoader {
     }
   }
 };
+
+// Work decomposition over the 8 XCDs. Workgroup id g runs on XCD g % 8, and
+// each XCD has its own L2, so every (b, h) head is kept on one XCD, where its
+// K/V re-reads stay in that L2. Within an XCD the block rank varies slowest
+// when the heads split evenly over the XCDs: the heaviest block of every head
+// starts before any lighter one, which keeps the tail of a causal launch
+// short. Otherwise each XCD takes a consecutive range of (head, rank) items.
+// The grid is 8 * ceil(heads * nblk / 8) workgroups.
+struct WorkItem {
+  int bh;    // b * H + h
+  int rank;  // 0 = first block to start
+  bool valid;
+};
+__device__ __forceinline__ WorkItem decode_work_item(int bid, int heads, int nblk) {
+  const int x = bid & 7;
+  const int i = bid >> 3;
+  if ((heads & 7) == 0) {
+    const int hpx = heads >> 3;
+    const int rank = i / hpx;
+    return {x * hpx + (i - rank * hpx), rank, rank < nblk};
+  }
+  const int total = heads * nblk;
+  const int item = x * ((total + 7) / 8) + i;
+  const int bh = item / nblk;
+  return {bh, item - bh * nblk, item < total};
+}
+
+// Workgroup execution barrier that waits for no outstanding memory operation.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 // 4-byte variant: lane l writes LDS bytes [lds_base + 4 l, +4).
 __device__ __forceinline__ void load_lds4(const void* src, void* lds_base) {
