@@ -178,14 +178,15 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
           dp[r] = 0.f;
         }
         const int rbase = sub * 32 * D * 2;
+        // The two accumulator chains are interleaved step by step: a single
+        // chain of dependent MFMAs cannot issue at the full rate.
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
+        for (int kk = 0; kk < KK; ++kk) {
           s = E::mfma(*(const u32x4*)(qb + rbase + roff[kk]),
                       *(const u32x4*)(ks0 + kvrow + roff[kk]), s);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
           dp = E::mfma(*(const u32x4*)(ob + rbase + roff[kk]),
                        *(const u32x4*)(vs0 + kvrow + roff[kk]), dp);
+        }
       };
       // P (masked), dropout, dS; packed as MFMA A operands for 16-query steps.
       // Register r holds query qbase + 8(r/4) + 4hh + r%4.
@@ -408,12 +409,13 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
         dp[r] = 0.f;
       }
       const int rbase = kb2 * 32 * D * 2;
+      // Interleaved chains: a single dependent MFMA chain cannot issue at
+      // the full rate.
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
+      for (int kk = 0; kk < KK; ++kk) {
         s = E::mfma(*(const u32x4*)(kb + rbase + roff[kk]), qf[kk], s);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
         dp = E::mfma(*(const u32x4*)(vb + rbase + roff[kk]), of[kk], dp);
+      }
       // dS^T = P^T (Z dP^T - D); register r is key k0 + 32kb2 + 8(r/4) + 4hh + r%4.
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
