@@ -249,16 +249,16 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
       auto step = [&](auto sub_c, const f32x16& s_c, const f32x16& dp_c, f32x16& s_n,
                       f32x16& dp_n) {
         constexpr int sub = decltype(sub_c)::value;
-        if (sub + 1 < NSUB) sdp(sub + 1, s_n, dp_n);
-        __builtin_amdgcn_sched_barrier(0);
         const int qbase = t * BQ + 32 * sub;
         const bool need_mask = (CAUSAL && qbase < kw + 31) || key_tail || (qbase + 32 > N);
         u32x4 pa[2], sa[2];
-        if (need_mask)
+        if (need_mask) {
+          if (sub + 1 < NSUB) sdp(sub + 1, s_n, dp_n);
           grad(sub, s_c, dp_c, pa, sa, std::true_type());
-        else
+        } else {
+          if (sub + 1 < NSUB) sdp(sub + 1, s_n, dp_n);
           grad(sub, s_c, dp_c, pa, sa, std::false_type());
-        __builtin_amdgcn_sched_barrier(0);
+        }
         dvdk(sub, pa, sa);
       };
       f32x16 s0, dp0, s1, dp1;
