@@ -183,10 +183,6 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
   a.B = p->B;
   a.H = p->H;
   a.N = p->N;
-  a.nkb = (p->N + attn::kBwdBlockK - 1) / attn::kBwdBlockK;
-  a.nqb = (p->N + attn::kBwdBlockQ - 1) / attn::kBwdBlockQ;
-  a.per_xcd_k = (p->B * p->H * a.nkb + 7) / 8;
-  a.per_xcd_q = (p->B * p->H * a.nqb + 7) / 8;
   a.scale = p->scale;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
   const bool dropout = p->dropout_p > 0.0f;

@@ -11,9 +11,10 @@
 //
 // Three kernels on the caller's stream:
 //   1. preprocess: D_i for every row (HBM-bound, 16 lanes per row).
-//   2. dK/dV: one workgroup per 128 keys (4 waves x 32 keys). K and V stay in
-//      VGPRs as MFMA B operands; Q, dO, lse and D stream through LDS in tiles of
-//      64 queries. Scores are computed as S = Q K^T so that each lane owns one
+//   2. dK/dV: one workgroup per 256 keys (8 waves x 32 keys, two waves per
+//      SIMD). K and V rows stay in LDS for the whole pass; Q and dO stream
+//      through LDS in tiles of 32 queries; lse and D come from L2 into
+//      registers. Scores are computed as S = Q K^T so that each lane owns one
 //      key and the query index runs along the accumulator registers: the fp32
 //      registers of P and dS, rounded to the input dtype, are then directly the
 //      A operands of dV = P^T dO and dK = dS^T Q, and dO and Q are fed as B
@@ -62,31 +63,31 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs 
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV. Workgroup: 128 keys of one (b, h); wave w owns keys kw .. kw+31.
-// The workgroup's K and V rows stay in LDS for the whole pass; Q and dO tiles
-// of 64 query rows (with their lse and D values) stream HBM -> LDS directly,
-// double-buffered, and are processed as two 32-row halves in a software
-// pipeline: the S and dP products of the next half are issued before the VALU
-// work of the current half, so the matrix cores run while P and dS are formed.
+// dK, dV. Workgroup: 8 waves x 32 keys = 256 keys of one (b, h), two waves per
+// SIMD. The workgroup's K and V rows stay in LDS for the whole pass; Q and dO
+// tiles of 32 query rows stream HBM -> LDS directly, double-buffered (for
+// d = 128 that fills the 160 KiB of LDS exactly); lse and D of the tile's rows
+// are read from L2 into registers.
+constexpr int kDkdvWaves = 8;
+constexpr int kDkdvThreads = 64 * kDkdvWaves;
+
 template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(const BwdArgs a) {
-  constexpr int BKW = 128;             // keys per workgroup
-  constexpr int BQ = 64;               // query rows per LDS tile
-  constexpr int NSUB = BQ / 32;
+  constexpr int NW = kDkdvWaves;
+  constexpr int BKW = 32 * NW;         // keys per workgroup
+  constexpr int BQ = 32;               // query rows per tile
   constexpr int KK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TILE_BYTES = BQ * D * 2;
   constexpr int KV_BYTES = BKW * D * 2;
+  constexpr int QW = (TILE_BYTES / 1024 < NW) ? TILE_BYTES / 1024 : NW;  // waves that load a tile
 
-  __shared__ __attribute__((aligned(1024)))
-      char smem[2 * KV_BYTES + 4 * TILE_BYTES + 4 * BQ * sizeof(float)];
-  char* const ks0 = smem;                                  // K rows of the block
-  char* const vs0 = smem + KV_BYTES;                       // V rows of the block
-  char* const qb0 = smem + 2 * KV_BYTES;                   // [2] Q tiles
-  char* const ob0 = qb0 + 2 * TILE_BYTES;                  // [2] dO tiles
-  float* const s_lse = (float*)(ob0 + 2 * TILE_BYTES);     // [2][BQ]
-  float* const s_del = s_lse + 2 * BQ;                     // [2][BQ]
+  __shared__ __attribute__((aligned(1024))) char smem[2 * KV_BYTES + 4 * TILE_BYTES];
+  char* const ks0 = smem;                        // K rows of the block
+  char* const vs0 = smem + KV_BYTES;             // V rows of the block
+  char* const qb0 = smem + 2 * KV_BYTES;         // [2] Q tiles
+  char* const ob0 = qb0 + 2 * TILE_BYTES;        // [2] dO tiles
 
   const int nkb = (a.N + BKW - 1) / BKW;
   const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, nkb);
@@ -127,21 +128,19 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
 
   if (k0 < kv_end) {
     const bool key_tail = kw + 32 > kv_end;
+    const bool wave_has_keys = kw < kv_end;
     const int qt0 = CAUSAL ? (k0 / BQ) : 0;
     const int nqt = (N + BQ - 1) / BQ;
     {
-      TilePairLoader<D, BKW, 4> kvload;
+      TilePairLoader<D, BKW, NW> kvload;
       kvload.init(w, lane);
       kvload.issue(K, V, k0, kv_end, ks0, vs0);
     }
-    TilePairLoader<D, BQ, 4> loader;
-    loader.init(w, lane);
-    // lse (wave 0) and D (wave 1) of the tile's rows, one dword per lane.
+    TilePairLoader<D, BQ, QW> loader;
+    if (w < QW) loader.init(w, lane);
     auto issue_tile = [&](int t, int buf) {
-      loader.issue(Q, dO, t * BQ, N, qb0 + buf * TILE_BYTES, ob0 + buf * TILE_BYTES);
-      const int row = min(t * BQ + lane, N - 1);
-      if (w == 0) load_lds4(LSE + row, s_lse + buf * BQ);
-      if (w == 1) load_lds4(DEL + row, s_del + buf * BQ);
+      if (w < QW)
+        loader.issue(Q, dO, t * BQ, N, qb0 + buf * TILE_BYTES, ob0 + buf * TILE_BYTES);
     };
 
     int roff[KK];     // row-read offsets (A operands and the K/V B operands)
@@ -165,45 +164,57 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
       __syncthreads();
       const int buf = (t - qt0) & 1;
       if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
+      const int qbase = t * BQ;
+      const bool active = wave_has_keys && (!CAUSAL || qbase + 31 >= kw);
+      if (!active) continue;
       const char* qb = qb0 + buf * TILE_BYTES;
       const char* ob = ob0 + buf * TILE_BYTES;
-      const float* lse_t = s_lse + buf * BQ;
-      const float* del_t = s_del + buf * BQ;
 
-      // S = Q K^T and dP = dO V^T for half `sub` (32 queries x 32 keys).
-      auto sdp = [&](int sub, f32x16& s, f32x16& dp) {
+      // lse and D of this lane's 16 query rows qbase + 8 g4 + 4 hh + e.
+      // Vector loads only where the rows are 16-byte aligned (N % 4 == 0).
+      f32x4 ls4[4], dl4[4];
+      const bool vec_rows = (N & 3) == 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.f;
-          dp[r] = 0.f;
-        }
-        const int rbase = sub * 32 * D * 2;
-        // The two accumulator chains are interleaved step by step: a single
-        // chain of dependent MFMAs cannot issue at the full rate.
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int q4 = qbase + 8 * g4 + 4 * hh;
+        if (vec_rows && q4 + 3 < N) {
+          ls4[g4] = *(const f32x4*)(LSE + q4);
+          dl4[g4] = *(const f32x4*)(DEL + q4);
+        } else {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          s = E::mfma(*(const u32x4*)(qb + rbase + roff[kk]),
-                      *(const u32x4*)(ks0 + kvrow + roff[kk]), s);
-          dp = E::mfma(*(const u32x4*)(ob + rbase + roff[kk]),
-                       *(const u32x4*)(vs0 + kvrow + roff[kk]), dp);
+          for (int e = 0; e < 4; ++e) {
+            const int qc = min(q4 + e, N - 1);
+            ls4[g4][e] = LSE[qc];
+            dl4[g4][e] = DEL[qc];
+          }
         }
-      };
+      }
+
+      // S = Q K^T and dP = dO V^T (32 queries x 32 keys), lane = key.
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s = E::mfma(*(const u32x4*)(qb + roff[kk]), *(const u32x4*)(ks0 + kvrow + roff[kk]), s);
+        dp = E::mfma(*(const u32x4*)(ob + roff[kk]), *(const u32x4*)(vs0 + kvrow + roff[kk]), dp);
+      }
+
       // P (masked), dropout, dS; packed as MFMA A operands for 16-query steps.
       // Register r holds query qbase + 8(r/4) + 4hh + r%4.
-      auto grad = [&](int sub, const f32x16& s, const f32x16& dp, u32x4 (&pa)[2],
-                      u32x4 (&sa)[2], auto masked) {
-        const int qbase = t * BQ + 32 * sub;
+      const bool need_mask = (CAUSAL && qbase < kw + 31) || key_tail || (qbase + 32 > N);
+      auto grad = [&](u32x4 (&pa)[2], u32x4 (&sa)[2], auto masked) {
         f32x16 pz, ds;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int ql = 32 * sub + 8 * g4 + 4 * hh;
-          const f32x4 ls4 = *(const f32x4*)&lse_t[ql];
-          const f32x4 dl4 = *(const f32x4*)&del_t[ql];
+        for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
             const int qi = qbase + 8 * g4 + 4 * hh + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[e] * kLog2e));
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[g4][e] * kLog2e));
             if (decltype(masked)::value) {
               const bool dead = (CAUSAL & (j > qi)) | (j >= kv_end) | (qi >= N);
               p = dead ? 0.f : p;
@@ -215,9 +226,8 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
               z = (u[j & 3] >= a.drop_threshold) ? a.drop_rescale : 0.f;
             }
             pz[r] = p * z;
-            ds[r] = p * (dp[r] * z - dl4[e]);
+            ds[r] = p * (dp[r] * z - dl4[g4][e]);
           }
-        }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -226,45 +236,26 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
             sa[c][e] = E::pack2(ds[8 * c + 2 * e], ds[8 * c + 2 * e + 1]);
           }
       };
-      // dV += (P Z)^T dO and dK += dS^T Q with dO, Q read transposed.
-      auto dvdk = [&](int sub, const u32x4 (&pa)[2], const u32x4 (&sa)[2]) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int tbase = (32 * sub + 16 * c) * D * 2;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const u32x2 olo = __builtin_bit_cast(u32x2, lds_read_tr16(ob, tbase + toff[0][db]));
-            const u32x2 ohi = __builtin_bit_cast(u32x2, lds_read_tr16(ob, tbase + toff[1][db]));
-            const u32x2 qlo = __builtin_bit_cast(u32x2, lds_read_tr16(qb, tbase + toff[0][db]));
-            const u32x2 qhi = __builtin_bit_cast(u32x2, lds_read_tr16(qb, tbase + toff[1][db]));
-            dv[db] = E::mfma(pa[c], u32x4{olo[0], olo[1], ohi[0], ohi[1]}, dv[db]);
-            dk[db] = E::mfma(sa[c], u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dk[db]);
-          }
-        }
-      };
+      u32x4 pa[2], sa[2];
+      if (need_mask)
+        grad(pa, sa, std::true_type());
+      else
+        grad(pa, sa, std::false_type());
 
-      // Two 32-row halves: the S/dP products of the second half are issued
-      // before the softmax-gradient arithmetic of the first.
-      static_assert(NSUB == 2, "the half pipeline below assumes 64-row tiles");
-      auto step = [&](auto sub_c, const f32x16& s_c, const f32x16& dp_c, f32x16& s_n,
-                      f32x16& dp_n) {
-        constexpr int sub = decltype(sub_c)::value;
-        const int qbase = t * BQ + 32 * sub;
-        const bool need_mask = (CAUSAL && qbase < kw + 31) || key_tail || (qbase + 32 > N);
-        u32x4 pa[2], sa[2];
-        if (need_mask) {
-          if (sub + 1 < NSUB) sdp(sub + 1, s_n, dp_n);
-          grad(sub, s_c, dp_c, pa, sa, std::true_type());
-        } else {
-          if (sub + 1 < NSUB) sdp(sub + 1, s_n, dp_n);
-          grad(sub, s_c, dp_c, pa, sa, std::false_type());
+      // dV += (P Z)^T dO and dK += dS^T Q with dO, Q read transposed.
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int tbase = 16 * c * D * 2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x2 olo = __builtin_bit_cast(u32x2, lds_read_tr16(ob, tbase + toff[0][db]));
+          const u32x2 ohi = __builtin_bit_cast(u32x2, lds_read_tr16(ob, tbase + toff[1][db]));
+          const u32x2 qlo = __builtin_bit_cast(u32x2, lds_read_tr16(qb, tbase + toff[0][db]));
+          const u32x2 qhi = __builtin_bit_cast(u32x2, lds_read_tr16(qb, tbase + toff[1][db]));
+          dv[db] = E::mfma(pa[c], u32x4{olo[0], olo[1], ohi[0], ohi[1]}, dv[db]);
+          dk[db] = E::mfma(sa[c], u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dk[db]);
         }
-        dvdk(sub, pa, sa);
-      };
-      f32x16 s0, dp0, s1, dp1;
-      sdp(0, s0, dp0);
-      step(std::integral_constant<int, 0>(), s0, dp0, s1, dp1);
-      step(std::integral_constant<int, 1>(), s1, dp1, s0, dp0);
+      }
     }
   }
 
@@ -486,10 +477,10 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 1) {
-    const int nkb = (a.N + 127) / 128;
+    const int nkb = (a.N + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
     const int tk = a.B * a.H * nkb;
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>),
-                       dim3(((tk + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
+                       dim3(((tk + 7) / 8) * 8), dim3(kDkdvThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

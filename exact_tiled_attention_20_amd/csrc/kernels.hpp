@@ -13,9 +13,8 @@ constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;
 constexpr int kFwdThreads = 256;
 
-// Backward tiling (dK/dV: 64 keys per workgroup; dQ: 128 queries per workgroup).
-constexpr int kBwdBlockK = 64;
-constexpr int kBwdBlockQ = 64;
+// dQ kernel: 4 waves x 32 query rows per workgroup (the dK/dV kernel's shape
+// is set next to it).
 constexpr int kBwdThreads = 256;
 
 struct FwdArgs {
@@ -51,10 +50,6 @@ struct BwdArgs {
   float* delta;          // workspace: D_i = dO_i . O_i, (B, H, N) fp32
   const int32_t* kv_len;
   int B, H, N;
-  int nkb;               // key blocks per head (dK/dV kernel)
-  int nqb;               // query blocks per head (dQ kernel)
-  int per_xcd_k;
-  int per_xcd_q;
   float scale;
   float scale_log2;
   uint32_t drop_threshold;
