@@ -16,6 +16,9 @@ Prints ONE JSON line. Options:
   --steps K     timed steps (default 10)
   --warmup W    untimed steps first (default 3)
   --no-cpu-baseline   skip timing the CPU oracle on its bounded sample
+  --no-per-config     skip the forward timings on each named workload (the
+                      `forward_per_config` field: median and minimum per
+                      launch, roofline fractions, one cold launch at N=4096)
 """
 from __future__ import annotations
 
@@ -96,12 +99,85 @@ def cpu_baseline(w, inputs, n_prefix: int = 16384, n_heads: int = 2) -> dict:
             "seconds": round(dt, 3)}
 
 
+def per_config_forward(attn, W, dev, reuse=None, min_iters=50, min_ms=200.0) -> dict:
+    """Forward alone on every named workload: 10 warm-up launches, then at
+    least min_iters launches and min_ms of GPU time, each bracketed by its own
+    HIP events on the launch stream; median and minimum per launch. Reports
+    nominal TFLOP/s (4BHN^2d, half under causal), for the padded workload also
+    the effective rate over visible pairs, the fraction of the dense bf16/fp16
+    peak, and the attainable roofline min(peak, AI x 8 TB/s) with AI the
+    algorithmic flop per byte (Q, K, V read once; O and lse written once).
+    For the N=4096 workload also one cold launch, after 512 MiB of device
+    writes have displaced it from the caches."""
+    import torch
+    out = {}
+    for name, w in W.WORKLOADS.items():
+        if reuse is not None and name in reuse:
+            q, k, v, kv = reuse[name]
+        else:
+            inp = W.make_inputs(w)
+            q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+            kv = None if inp.kv_len is None else inp.kv_len.to(dev)
+        seed = W.DROPOUT_SEED if w.dropout_p > 0 else 0
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+        def launch():
+            attn.fwd(q, k, v, causal=w.causal, kv_len=kv, dropout_p=w.dropout_p, seed=seed,
+                     scale=w.scale, out=o, lse=lse)
+
+        for _ in range(10):
+            launch()
+        torch.cuda.synchronize()
+        times = []
+        while len(times) < min_iters or sum(times) < min_ms:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(min_iters)]
+            for e0, e1 in evs:
+                e0.record()
+                launch()
+                e1.record()
+            torch.cuda.synchronize()
+            times += [e0.elapsed_time(e1) for e0, e1 in evs]
+        times.sort()
+        med, mn = times[len(times) // 2], times[0]
+        flops = w.flops_fwd()
+        elt = 2
+        nbytes = 4 * w.B * w.H * w.N * w.d * elt + 4 * w.B * w.H * w.N
+        ai = flops / nbytes
+        attainable = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1000.0)
+        tf = flops / (med * 1e-3) / 1e12
+        rec = {"launches": len(times), "median_ms": round(med, 5), "min_ms": round(mn, 5),
+               "tflops": round(tf, 2), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+               "ai_flop_per_byte": round(ai, 1), "attainable_tflops": round(attainable, 1),
+               "frac_of_attainable": round(tf / attainable, 4)}
+        if kv is not None:
+            vis = float(kv.double().clamp(0, w.N).sum().item()) / (w.B * w.N)
+            rec["effective_tflops"] = round(tf * vis, 2)
+            rec["visible_key_fraction"] = round(vis, 4)
+        if name == "long_b4h16n4096d128_bf16_causal":
+            scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+            scratch.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            rec["cold_ms"] = round(e0.elapsed_time(e1), 5)
+            del scratch
+        out[name] = rec
+        del o, lse
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip timing the forward on each named workload")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only the forward headline workload (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -266,6 +342,9 @@ def main() -> int:
         "roofline": roof,
         "csrc_digest": _csrc_digest(),
     }
+    if not args.no_per_config:
+        out["forward_per_config"] = per_config_forward(
+            attn, W, dev, reuse={WORKLOAD: (q, k, v, None)})
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs)
     print(json.dumps(out))
