@@ -91,10 +91,12 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
       k0 += kPhiloxW0;
       k1 += kPhiloxW1;
     }
-    const uint32_t hi0 = __umulhi(kPhiloxM0, c[0]);
-    const uint32_t lo0 = kPhiloxM0 * c[0];
-    const uint32_t hi1 = __umulhi(kPhiloxM1, c[2]);
-    const uint32_t lo1 = kPhiloxM1 * c[2];
+    // One 32x32 -> 64-bit multiply per product (v_mad_u64_u32) gives both
+    // halves the round needs.
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * c[0];
+    const uint64_t p1 = (uint64_t)kPhiloxM1 * c[2];
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
     u32x4 n;
     n[0] = hi1 ^ c[1] ^ k0;
     n[1] = lo1;
