@@ -29,6 +29,8 @@
 //     same XCD (workgroup ids are dispatched round-robin over the 8 XCDs), which
 //     keeps that head's K/V re-reads in one L2; under a causal mask the
 //     heaviest (last) query blocks of all of an XCD's heads start first.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -136,11 +138,14 @@ void attn_fwd_kernel(const FwdArgs a) {
 
   if (ntiles > 0) issue_tile(0, 0);
 
-  for (int t = 0; t < ntiles; ++t) {
+  // The loop body is instantiated once per buffer (the loop is unrolled by
+  // two), so every LDS address is a per-lane offset plus a constant that the
+  // read instructions carry as their immediate offset.
+  auto tile_step = [&](int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     // Tile t has landed in LDS once every wave's copies are complete.
     wait_all_memory();
     __syncthreads();
-    const int buf = t & 1;
     const bool more = (t + 1) < ntiles;
     // Buffer buf^1 was last read in iteration t-1, which every wave has left.
     if (more) issue_tile(t + 1, buf ^ 1);
@@ -252,6 +257,10 @@ void attn_fwd_kernel(const FwdArgs a) {
         }
       }
     }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>());
+    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
   }
 
   // Epilogue: O = O_acc / lr (times 1/(1-p) under dropout), lse = m + ln l.
