@@ -159,14 +159,16 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     const float c2 = a.scale_log2;
 
     if (qt0 < nqt) issue_tile(qt0, 0);
-    for (int t = qt0; t < nqt; ++t) {
+    // Unrolled by two (one instantiation per buffer), so LDS addresses carry
+    // the buffer offset as an immediate.
+    auto tile_step = [&](int t, auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;
       wait_all_memory();
       __syncthreads();
-      const int buf = (t - qt0) & 1;
       if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
       const int qbase = t * BQ;
       const bool active = wave_has_keys && (!CAUSAL || qbase + 31 >= kw);
-      if (!active) continue;
+      if (!active) return;
       const char* qb = qb0 + buf * TILE_BYTES;
       const char* ob = ob0 + buf * TILE_BYTES;
 
@@ -256,6 +258,10 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
           dk[db] = E::mfma(sa[c], u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dk[db]);
         }
       }
+    };
+    for (int t = qt0; t < nqt; t += 2) {
+      tile_step(t, std::integral_constant<int, 0>());
+      if (t + 1 < nqt) tile_step(t + 1, std::integral_constant<int, 1>());
     }
   }
 
@@ -374,10 +380,13 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   const float c2 = a.scale_log2;
 
   if (ntiles > 0) loader.issue(K, V, 0, kv_end, kb0, vb0);
-  for (int t = 0; t < ntiles; ++t) {
+  // The loop body is instantiated once per buffer (the loop is unrolled by
+  // two), so every LDS address is a per-lane offset plus a constant that the
+  // read instructions carry as their immediate offset.
+  auto tile_step = [&](int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     wait_all_memory();
     __syncthreads();
-    const int buf = t & 1;
     // Untracked, so that no LDS read of tile t waits for this prefetch; the
     // wait at the top of the next iteration orders it before its readers.
     if (t + 1 < ntiles) {
@@ -386,7 +395,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
     }
     const int k0 = t * BC;
     const bool active = wave_has_rows && (!CAUSAL || k0 <= wq0 + 31);
-    if (!active) continue;
+    if (!active) return;
     const char* kb = kb0 + buf * TILE_BYTES;
     const char* vb = vb0 + buf * TILE_BYTES;
     const bool need_mask = (CAUSAL && (k0 + BC - 1 > wq0)) || (k0 + BC > kv_end);
@@ -443,6 +452,10 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
         }
       }
     }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>());
+    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
   }
 
   if (qi < N) {
