@@ -135,8 +135,9 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
 
 size_t attn_bwd_workspace_bytes(const attn_params* p) {
   if (check_params(p) != ATTN_OK) return 0;
-  // D_i = dO_i . O_i in fp32, (B, H, N), rounded up to 256 bytes.
-  return (stat_bytes(p) + 255) & ~size_t(255);
+  // Two fp32 (B, H, N) arrays, each rounded up to 256 bytes: D_i = dO_i . O_i
+  // and lse_i * log2(e).
+  return 2 * ((stat_bytes(p) + 255) & ~size_t(255));
 }
 
 static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, const void* k,
@@ -179,6 +180,8 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
   a.dk = dk;
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    ((stat_bytes(p) + 255) & ~size_t(255)));
   a.kv_len = p->kv_len;
   a.B = p->B;
   a.H = p->H;

@@ -38,7 +38,10 @@ __device__ __forceinline__ float load_out(const void* p, size_t idx) {
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO[i][c] * O[i][c]. D/8 lanes per row, 8 elements per lane.
+// D_i = sum_c dO[i][c] * O[i][c], and lse_i in log2 units (the form the
+// dK/dV kernel subtracts from its exponents; +inf for a row without visible
+// keys, so that its probabilities come out 0). D/8 lanes per row, 8 elements
+// per lane.
 template <typename E, int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs a) {
   constexpr int LPR = D / 8;  // lanes per row
@@ -59,7 +62,11 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs 
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) a.delta[row] = acc;
+  if (row < rows && part == 0) {
+    a.delta[row] = acc;
+    const float x = a.lse[row];
+    a.lse2[row] = (x == -INFINITY) ? INFINITY : x * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -102,7 +109,7 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   const uint16_t* __restrict__ K = a.k + head;
   const uint16_t* __restrict__ V = a.v + head;
   const uint16_t* __restrict__ dO = a.d_o + head;
-  const float* __restrict__ LSE = a.lse + (size_t)bh * N;
+  const float* __restrict__ LSE = a.lse2 + (size_t)bh * N;  // lse * log2(e)
   const float* __restrict__ DEL = a.delta + (size_t)bh * N;
 
   const int tid = threadIdx.x;
@@ -172,7 +179,8 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
       const char* qb = qb0 + buf * TILE_BYTES;
       const char* ob = ob0 + buf * TILE_BYTES;
 
-      // lse and D of this lane's 16 query rows qbase + 8 g4 + 4 hh + e.
+      // lse (in log2 units) and D of this lane's 16 query rows
+      // qbase + 8 g4 + 4 hh + e.
       // Vector loads only where the rows are 16-byte aligned (N % 4 == 0).
       f32x4 ls4[4], dl4[4];
       const bool vec_rows = (N & 3) == 0;
@@ -216,7 +224,7 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
             const int qi = qbase + 8 * g4 + 4 * hh + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[g4][e] * kLog2e));
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[g4][e]));
             if (decltype(masked)::value) {
               const bool dead = (CAUSAL & (j > qi)) | (j >= kv_end) | (qi >= N);
               p = dead ? 0.f : p;

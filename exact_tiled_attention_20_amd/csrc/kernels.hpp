@@ -48,6 +48,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;          // workspace: D_i = dO_i . O_i, (B, H, N) fp32
+  float* lse2;           // workspace: lse_i * log2(e) (+inf where lse_i = -inf), (B, H, N) fp32
   const int32_t* kv_len;
   int B, H, N;
   float scale;

@@ -113,7 +113,8 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
 /* The three steps attn_bwd enqueues, callable one at a time (same arguments
  * and validation as attn_bwd; each ignores the outputs it does not write).
  * Calling them in this order on one stream equals attn_bwd:
- *   ATTN_BWD_STAGE_PREPROCESS  D_i = dO_i . O_i into the workspace
+ *   ATTN_BWD_STAGE_PREPROCESS  D_i = dO_i . O_i and lse_i * log2(e) into the
+ *                              workspace
  *   ATTN_BWD_STAGE_DKDV        dK, dV (reads the workspace)
  *   ATTN_BWD_STAGE_DQ          dQ     (reads the workspace)
  * Useful for timing each kernel with events, or for overlapping dQ with

@@ -142,7 +142,8 @@ def test_fwd_rejects_aliasing(lib):
 def test_bwd_workspace_checks(lib):
     p = _params()
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(p))
-    assert need == ((2 * 3 * 100 * 4 + 255) // 256) * 256
+    # two fp32 (B, H, N) arrays (D and lse in log2 units), each 256-byte rounded
+    assert need == 2 * (((2 * 3 * 100 * 4 + 255) // 256) * 256)
     ptrs = _ptrs(10)
     assert _bwd(lib, p, ptrs, ws_bytes=need - 1) == 3
     bad = list(ptrs)
