@@ -90,11 +90,15 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int KV_BYTES = BKW * D * 2;
   constexpr int QW = (TILE_BYTES / 1024 < NW) ? TILE_BYTES / 1024 : NW;  // waves that load a tile
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * KV_BYTES + 4 * TILE_BYTES];
-  char* const ks0 = smem;                        // K rows of the block
-  char* const vs0 = smem + KV_BYTES;             // V rows of the block
-  char* const qb0 = smem + 2 * KV_BYTES;         // [2] Q tiles
-  char* const ob0 = qb0 + 2 * TILE_BYTES;        // [2] dO tiles
+  // LDS: the Q and dO tiles first (within reach of the 16-bit immediate
+  // offset of LDS reads), then one block per wave holding that wave's 32 K
+  // rows followed by its 32 V rows, so both are addressed from one per-lane
+  // base.
+  constexpr int KV_WAVE = 32 * D * 2;            // K (or V) rows of one wave
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES + 2 * KV_BYTES];
+  char* const qb0 = smem;                        // [2] Q tiles
+  char* const ob0 = smem + 2 * TILE_BYTES;       // [2] dO tiles
+  constexpr int KVB = 4 * TILE_BYTES;            // byte offset of the per-wave K/V blocks
 
   const int nkb = (a.N + BKW - 1) / BKW;
   const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, nkb);
@@ -139,9 +143,12 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     const int qt0 = CAUSAL ? (k0 / BQ) : 0;
     const int nqt = (N + BQ - 1) / BQ;
     {
+      // Wave w's slices of the 256-row K/V block are exactly its own 32 keys.
       TilePairLoader<D, BKW, NW> kvload;
+      static_assert(TilePairLoader<D, BKW, NW>::SPW * 1024 == KV_WAVE, "one block per wave");
       kvload.init(w, lane);
-      kvload.issue(K, V, k0, kv_end, ks0, vs0);
+      char* const mine = smem + KVB + w * 2 * KV_WAVE;
+      kvload.issue_local(K, V, k0, kv_end, mine, mine + KV_WAVE);
     }
     TilePairLoader<D, BQ, QW> loader;
     if (w < QW) loader.init(w, lane);
@@ -153,7 +160,9 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     int roff[KK];     // row-read offsets (A operands and the K/V B operands)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) roff[kk] = lds_off<D>(l32, (kk * 2 + hh) * 16);
-    const int kvrow = 32 * w * D * 2;   // this wave's 32 key rows inside ks0 / vs0
+    int kvoff[KK];    // the same reads in this wave's K block (V: + KV_WAVE)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kvoff[kk] = KVB + w * 2 * KV_WAVE + roff[kk];
     const int g = lane >> 4;
     const int i16 = lane & 15;
     int toff[2][NDB];
@@ -209,8 +218,9 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        s = E::mfma(*(const u32x4*)(qb + roff[kk]), *(const u32x4*)(ks0 + kvrow + roff[kk]), s);
-        dp = E::mfma(*(const u32x4*)(ob + roff[kk]), *(const u32x4*)(vs0 + kvrow + roff[kk]), dp);
+        s = E::mfma(*(const u32x4*)(qb + roff[kk]), *(const u32x4*)(smem + kvoff[kk]), s);
+        dp = E::mfma(*(const u32x4*)(ob + roff[kk]),
+                     *(const u32x4*)(smem + kvoff[kk] + KV_WAVE), dp);
       }
 
       // P (masked), dropout, dS; packed as MFMA A operands for 16-query steps.

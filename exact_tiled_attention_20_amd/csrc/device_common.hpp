@@ -229,6 +229,22 @@ struct TilePairLoader {
       load_lds16(at + off, lds + (wave * SPW + u) * 1024);
     }
   }
+  // Like issue(), but slice u of this wave goes to lds_a / lds_b + u * 1024:
+  // the caller passes this wave's own destination blocks.
+  __device__ __forceinline__ void issue_local(const uint16_t* A, const uint16_t* B, int row0,
+                                              int valid, char* lds_a, char* lds_b) const {
+    const char* at = (const char*)A + (size_t)row0 * D * 2;
+    const char* bt = (const char*)B + (size_t)row0 * D * 2;
+    const bool partial = row0 + ROWS > valid;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      uint32_t off = goff[u];
+      if (partial && row0 + grow[u] >= valid)
+        off += (uint32_t)((valid - 1 - row0 - grow[u]) * D * 2);
+      load_lds16(at + off, lds_a + u * 1024);
+      load_lds16(bt + off, lds_b + u * 1024);
+    }
+  }
   // Tile rows [row0, row0 + ROWS) of A and B into lds_a / lds_b.
   __device__ __forceinline__ void issue(const uint16_t* A, const uint16_t* B, int row0,
                                         int valid, char* lds_a, char* lds_b) const {
