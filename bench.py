@@ -299,8 +299,9 @@ def main() -> int:
     for name, ms in zip(KERNEL_NAMES, per_kernel):
         kernels[name] = {"avg_ms": round(ms, 4),
                          "alg_tflops": round(alg[name] / (ms * 1e-3) / 1e12, 2) if alg[name] else None}
-    # The preprocess kernel is HBM-bound: it reads dO and O, writes D.
-    pre_bytes = 2 * q.numel() * 2 + lse.numel() * 4
+    # The preprocess kernel is HBM-bound: it reads dO, O and lse, and writes D
+    # and lse in log2 units.
+    pre_bytes = 2 * q.numel() * 2 + lse.numel() * 12
     kernels["attn_bwd_preprocess_kernel"]["gbs"] = round(pre_bytes / (per_kernel[1] * 1e-3) / 1e9, 1)
     dom = max(range(4), key=lambda j: per_kernel[j])
     dom_name = KERNEL_NAMES[dom]
