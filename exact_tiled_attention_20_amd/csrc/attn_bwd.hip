@@ -435,26 +435,34 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
         dp = E::mfma(*(const u32x4*)(vb + rbase + roff[kk]), of[kk], dp);
       }
       // dS^T = P^T (Z dP^T - D); register r is key k0 + 32kb2 + 8(r/4) + 4hh + r%4.
+      // The masked form is a separate instantiation, so the unmasked tiles
+      // run branch-free.
+      auto grad = [&](auto masked) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int j0 = k0 + kb2 * 32 + 8 * g4 + 4 * hh;
-        u32x4 u = u32x4{0, 0, 0, 0};
-        if (DROPOUT)
-          u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h, (uint32_t)b,
-                            a.seed_lo, a.seed_hi);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int j0 = k0 + kb2 * 32 + 8 * g4 + 4 * hh;
+          u32x4 u = u32x4{0, 0, 0, 0};
+          if (DROPOUT)
+            u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h, (uint32_t)b,
+                              a.seed_lo, a.seed_hi);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
-          if (need_mask) {
-            const int jj = j0 + e;
-            if ((CAUSAL && jj > qi) || jj >= kv_end) p = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
+            if (decltype(masked)::value) {
+              const int jj = j0 + e;
+              p = ((CAUSAL && jj > qi) || jj >= kv_end) ? 0.f : p;
+            }
+            float dpz = dp[r];
+            if (DROPOUT) dpz = (u[e] >= a.drop_threshold) ? dpz * a.drop_rescale : 0.f;
+            s[r] = p * (dpz - dlt);
           }
-          float dpz = dp[r];
-          if (DROPOUT) dpz = (u[e] >= a.drop_threshold) ? dpz * a.drop_rescale : 0.f;
-          s[r] = p * (dpz - dlt);
         }
-      }
+      };
+      if (need_mask)
+        grad(std::true_type());
+      else
+        grad(std::false_type());
       // dQ^T += K^T dS^T, two 16-key MFMA steps.
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
