@@ -90,17 +90,13 @@ void attn_fwd_kernel(const FwdArgs a) {
   char* const kb0 = smem;
   char* const vb0 = smem + 2 * TILE_BYTES;
 
-  // K/V tiles are copied HBM -> LDS directly, in the swizzled layout.
+  // K/V tiles are copied HBM -> LDS directly, in the swizzled layout. The
+  // copies are issued untracked: the compiler would otherwise make the first
+  // LDS read after them wait for their completion, which would serialise the
+  // prefetch with the products of the current tile. The wait at the top of
+  // each iteration orders them before every read of their buffer.
   TilePairLoader<D, BC, 4> loader;
   loader.init(w, lane);
-  // The copies are issued untracked: the compiler would otherwise make the
-  // first LDS read after them wait for their completion, which would serialise
-  // the prefetch of tile t+1 with the PV product of tile t. The wait at the
-  // top of each iteration orders them before every read of their buffer.
-  auto issue_tile = [&](int t, int buf) {
-    loader.issue_one_untracked(K, t * BC, kv_end, kb0 + buf * TILE_BYTES);
-    loader.issue_one_untracked(V, t * BC, kv_end, vb0 + buf * TILE_BYTES);
-  };
 
   // Loop-invariant LDS offsets. The swizzle depends only on the low four row
   // bits, so moving by 32 K rows or 16 V rows is a plain byte offset.
@@ -136,131 +132,223 @@ void attn_fwd_kernel(const FwdArgs a) {
   const float c2 = a.scale_log2;
   const float thr = a.rescale_thr;
 
-  if (ntiles > 0) issue_tile(0, 0);
+  // Tiles this wave computes: under a causal mask a wave stops at the tile
+  // holding its last row's diagonal (it keeps meeting the barriers).
+  int ntiles_w = wave_has_rows ? ntiles : 0;
+  if (CAUSAL) ntiles_w = min(ntiles_w, (wq0 + 31) / BC + 1);
 
-  // The loop body is instantiated once per buffer (the loop is unrolled by
-  // two), so every LDS address is a per-lane offset plus a constant that the
-  // read instructions carry as their immediate offset.
-  auto tile_step = [&](int t, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    // Tile t has landed in LDS once every wave's copies are complete.
+  // Scores of one tile: S^T = K Q^T, 32 keys x 32 queries per block. The
+  // NKB accumulator chains are interleaved step by step: a single chain of
+  // dependent MFMAs cannot issue at the full rate.
+  auto scores = [&](const char* kb, f32x16 (&s)[NKB], auto&& after_step) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb2][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
+        s[kb2] = E::mfma(*(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk]), qf[kk], s[kb2]);
+      after_step(kk);
+    }
+  };
+  auto no_hook = [](int) {};
+  // Mask (causal diagonal tiles, the ragged tail, key padding) of the tile
+  // starting at key k0, and the row maximum of a tile.
+  auto mask = [&](f32x16 (&s)[NKB], int k0) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = k0 + kb2 * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const bool dead = (CAUSAL && j > qi) || (j >= kv_end);
+        if (dead) s[kb2][r] = -INFINITY;
+      }
+  };
+  auto row_max = [&](const f32x16 (&s)[NKB]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
+    return halves_max(mx);
+  };
+  auto need_mask = [&](int k0) {
+    return (CAUSAL && (k0 + BC - 1 > wq0)) || (k0 + BC > kv_end);
+  };
+  // Online softmax, lazy form: the reference is raised only when the tile's
+  // row maximum exceeds it by more than the threshold.
+  auto rescale = [&](float mx) {
+    const bool raise = mx > m_ref + thr;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * c2) : 1.f;
+      if (raise) m_ref = mx;
+      l *= alpha;
+      lr *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+  };
+
+  // Scores of tile t (raw q.k) live in ss[t & 1]: iteration t reads one set
+  // and fills the other, so no copy is needed between iterations.
+  f32x16 ss[2][NKB];
+  if (ntiles > 0) {
+    loader.issue_one_untracked(K, 0, kv_end, kb0);
+    loader.issue_one_untracked(V, 0, kv_end, vb0);
     wait_all_memory();
     __syncthreads();
-    const bool more = (t + 1) < ntiles;
-    // Buffer buf^1 was last read in iteration t-1, which every wave has left.
-    if (more) issue_tile(t + 1, buf ^ 1);
+    if (ntiles > 1) loader.issue_one_untracked(K, BC, kv_end, kb0 + TILE_BYTES);
+    if (ntiles_w > 0) {
+      scores(kb0, ss[0], no_hook);
+      if (need_mask(0)) mask(ss[0], 0);
+      rescale(row_max(ss[0]));
+    }
+  }
+
+  // Iteration t: P(t) = exp(S(t) - m) times V(t). The MFMAs of
+  // S(t+1) = K(t+1) Q^T run beside the exponentials of tile t, and the row
+  // maximum of tile t+1 (with the reference update it triggers) beside the PV
+  // MFMAs. K(t) and V(t) live in buffer t & 1 of their region; K runs one tile
+  // ahead of V. After a wave's last tile the scores of the next one are formed
+  // from whatever that buffer holds and discarded, which keeps the body one
+  // straight-line block.
+  // With SPREAD the copies of K(t+2) and V(t+1) (both full tiles) are issued
+  // one slice per k-step of the S(t+1) product instead of all at once: a burst
+  // of tile copies from every wave of the CU stalls each wave at the issue.
+  constexpr int SPW = TilePairLoader<D, BC, 4>::SPW;
+  auto body = [&](int t, auto buf_c, auto spread_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr bool SPREAD = decltype(spread_c)::value;
+    f32x16 (&sc)[NKB] = ss[buf];
+    f32x16 (&sn)[NKB] = ss[buf ^ 1];
     const int k0 = t * BC;
-    const bool active = wave_has_rows && (!CAUSAL || k0 <= wq0 + 31);
-    if (active) {
-      const char* kb = kb0 + buf * TILE_BYTES;
-      const char* vb = vb0 + buf * TILE_BYTES;
-      // S^T = K Q^T, 32 keys x 32 queries per block.
-      // The NKB accumulator chains are interleaved step by step: a single
-      // chain of dependent MFMAs cannot issue at the full rate.
-      f32x16 s[NKB];
-#pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb2][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-          s[kb2] = E::mfma(*(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk]), qf[kk], s[kb2]);
-      // Mask: causal diagonal tiles, the ragged tail and key padding.
-      const bool need_mask = (CAUSAL && (k0 + BC - 1 > wq0)) || (k0 + BC > kv_end);
-      if (need_mask) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = k0 + kb2 * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool dead = (CAUSAL && j > qi) || (j >= kv_end);
-            if (dead) s[kb2][r] = -INFINITY;
-          }
-      }
-      // Online softmax (log2 domain for v_exp_f32).
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
-      mx = halves_max(mx);
-      const bool raise = mx > m_ref + thr;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mx) * c2) : 1.f;
-        if (raise) m_ref = mx;
-        l *= alpha;
-        lr *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      }
-      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c2, -mb));
-          rs += p;
-          s[kb2][r] = p;
+    const char* kbn = kb0 + (buf ^ 1) * TILE_BYTES;
+    const char* vb = vb0 + buf * TILE_BYTES;
+    scores(kbn, sn, [&](int kk) {
+      if constexpr (SPREAD) {
+        constexpr int per = KK / (2 * SPW) > 0 ? KK / (2 * SPW) : 1;
+        if (kk % per == 0 && kk / per < 2 * SPW) {
+          const int i = kk / per;
+          if (i < SPW)
+            loader.issue_slice_full(K, (t + 2) * BC, kb0 + buf * TILE_BYTES, i);
+          else
+            loader.issue_slice_full(V, (t + 1) * BC, vb0 + (buf ^ 1) * TILE_BYTES, i - SPW);
         }
-      l += rs;
-      // P^T as MFMA B operands: 16 keys per step, 8 per lane.
-      u32x4 pf[NC16];
-      float rr_sum = 0.f;
+      }
+    });
+    // Probabilities of tile t (log2 domain for v_exp_f32).
+    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb2][r], c2, -mb));
+        rs += p;
+        sc[kb2][r] = p;
+      }
+    l += rs;
+    // P^T as MFMA B operands: 16 keys per step, 8 per lane.
+    u32x4 pf[NC16];
+    float rr_sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC16; ++c) {
+      const int kb2 = c >> 1;
+      const int rr = (c & 1) * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[c][e] = E::pack2(sc[kb2][rr + 2 * e], sc[kb2][rr + 2 * e + 1]);
+        rr_sum = E::add_pair(pf[c][e], rr_sum);
+      }
+    }
+    lr += rr_sum;
+    if (DROPOUT) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int j0 = k0 + kb2 * 32 + 8 * g4 + 4 * hh;
+          const u32x4 u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h,
+                                        (uint32_t)b, a.seed_lo, a.seed_hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (u[e] < a.drop_threshold) sc[kb2][4 * g4 + e] = 0.f;
+        }
 #pragma unroll
       for (int c = 0; c < NC16; ++c) {
         const int kb2 = c >> 1;
         const int rr = (c & 1) * 8;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pf[c][e] = E::pack2(s[kb2][rr + 2 * e], s[kb2][rr + 2 * e + 1]);
-          rr_sum = E::add_pair(pf[c][e], rr_sum);
-        }
-      }
-      lr += rr_sum;
-      if (DROPOUT) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int j0 = k0 + kb2 * 32 + 8 * g4 + 4 * hh;
-            const u32x4 u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h,
-                                          (uint32_t)b, a.seed_lo, a.seed_hi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (u[e] < a.drop_threshold) s[kb2][4 * g4 + e] = 0.f;
-          }
-#pragma unroll
-        for (int c = 0; c < NC16; ++c) {
-          const int kb2 = c >> 1;
-          const int rr = (c & 1) * 8;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pf[c][e] = E::pack2(s[kb2][rr + 2 * e], s[kb2][rr + 2 * e + 1]);
-        }
-      }
-      // O^T += V^T P^T. Lane (group g = lane/16, i = lane%16) addresses row
-      // 16c + 4hh + i/4 (+8) and columns 32db + 16(g&1) + 4(i&3) .. +4.
-#pragma unroll
-      for (int c = 0; c < NC16; ++c) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x2 lo = __builtin_bit_cast(
-              u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[0][db]));
-          const u32x2 hi = __builtin_bit_cast(
-              u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[1][db]));
-          acc[db] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[c], acc[db]);
-        }
+        for (int e = 0; e < 4; ++e)
+          pf[c][e] = E::pack2(sc[kb2][rr + 2 * e], sc[kb2][rr + 2 * e + 1]);
       }
     }
+    // O^T += V^T P^T. Lane (group g = lane/16, i = lane%16) addresses row
+    // 16c + 4hh + i/4 (+8) and columns 32db + 16(g&1) + 4(i&3) .. +4.
+#pragma unroll
+    for (int c = 0; c < NC16; ++c) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2 lo = __builtin_bit_cast(
+            u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[0][db]));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[1][db]));
+        acc[db] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[c], acc[db]);
+      }
+    }
+    // Maximum of tile t+1 beside the PV MFMAs; a tile that needs a mask is
+    // masked afterwards and its maximum taken again. After a wave's last tile
+    // the next scores are not real.
+    float mx = row_max(sn);
+    if (need_mask(k0 + BC)) {
+      mask(sn, k0 + BC);
+      mx = row_max(sn);
+    }
+    if (t + 1 < ntiles_w) rescale(mx);
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    tile_step(t, std::integral_constant<int, 0>());
-    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
+
+  // The loop body is instantiated once per buffer (the loop is unrolled by
+  // two), so every LDS address is a per-lane offset plus a constant that the
+  // read instructions carry as their immediate offset.
+  auto tile_step = [&](int t, auto buf_c, auto spread_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr bool SPREAD = decltype(spread_c)::value;
+    // K(t+1) and V(t) have landed once every wave's copies are complete.
+    wait_all_memory();
+    __syncthreads();
+    // K(t) was last read in iteration t-1 and V(t-1) there too, which every
+    // wave has left.
+    if constexpr (!SPREAD) {
+      if (t + 2 < ntiles)
+        loader.issue_one_untracked(K, (t + 2) * BC, kv_end, kb0 + buf * TILE_BYTES);
+      if (t + 1 < ntiles)
+        loader.issue_one_untracked(V, (t + 1) * BC, kv_end, vb0 + (buf ^ 1) * TILE_BYTES);
+    }
+    if (t < ntiles_w) {
+      body(t, buf_c, spread_c);
+    } else if constexpr (SPREAD) {
+      loader.issue_one_untracked(K, (t + 2) * BC, kv_end, kb0 + buf * TILE_BYTES);
+      loader.issue_one_untracked(V, (t + 1) * BC, kv_end, vb0 + (buf ^ 1) * TILE_BYTES);
+    }
+  };
+  // Iterations t < tsp copy two full tiles (K(t+2) and V(t+1)) and spread
+  // them; the last few iterations copy the possibly partial tail at the top.
+  const int tsp = max(0, min(ntiles - 2, kv_end / BC - 2));
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t + 1 < tsp; t += 2) {
+    tile_step(t, C0(), std::true_type());
+    tile_step(t + 1, C1(), std::true_type());
+  }
+  // t is even here.
+  for (; t < ntiles; t += 2) {
+    tile_step(t, C0(), std::false_type());
+    if (t + 1 < ntiles) tile_step(t + 1, C1(), std::false_type());
   }
 
   // Epilogue: O = O_acc / lr (times 1/(1-p) under dropout), lse = m + ln l.

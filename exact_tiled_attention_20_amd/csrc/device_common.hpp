@@ -216,6 +216,14 @@ struct TilePairLoader {
       load_lds16_untracked(at, off, lds + (wave * SPW + u) * 1024);
     }
   }
+  // Slice u of a full tile (every row below `valid`), untracked like
+  // issue_one_untracked: lets a caller spread one tile's copies over a stretch
+  // of other work.
+  __device__ __forceinline__ void issue_slice_full(const uint16_t* A, int row0, char* lds,
+                                                   int u) const {
+    const char* at = (const char*)A + (size_t)row0 * D * 2;
+    load_lds16_untracked(at, goff[u], lds + (wave * SPW + u) * 1024);
+  }
   // Tile rows [row0, row0 + ROWS) of one array into lds.
   __device__ __forceinline__ void issue_one(const uint16_t* A, int row0, int valid,
                                             char* lds) const {
