@@ -65,6 +65,31 @@ def _traffic_for(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def _clock_for(kernel: str, workload: str):
+    """Average shader clock (MHz) while the kernel ran, from committed rocprofv3
+    counter runs (active cycles over the same dispatches' durations), if they
+    were taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "clock.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(f"{kernel}@{workload}")
+    if not rec or rec.get("csrc_digest") != _csrc_digest():
+        return None
+    return rec.get("avg_clock_mhz")
+
+
+def _at_clock(tflops: float, mhz):
+    """The dense bf16 peak scales with the clock: the datasheet figure is
+    quoted at 2400 MHz."""
+    if mhz is None:
+        return None
+    peak = PEAK_BF16_TFLOPS * mhz / 2400.0
+    return {"avg_clock_mhz": mhz, "peak_tflops_at_clock": round(peak, 1),
+            "pct_of_clock_peak": round(100 * tflops / peak, 2)}
+
+
 def cpu_baseline(w, inputs, n_prefix: int = 16384, n_heads: int = 2) -> dict:
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
     the first n_heads heads of batch 0, over the causal prefix of the first
@@ -315,6 +340,13 @@ def main() -> int:
         roof = {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = _traffic_for(dom_name, WORKLOAD)
+    fwd_tflops = f_fwd / (per_kernel[0] * 1e-3) / 1e12
+    # The same figures against the peak at the clock the chip actually ran.
+    clock = {"source": "profiles/clock.json (rocprofv3 counters on these kernel sources)",
+             "fwd": _at_clock(fwd_tflops, _clock_for("attn_fwd_kernel", WORKLOAD)),
+             "fwd_long": _at_clock(fwd_long_tflops, _clock_for("attn_fwd_kernel", FWD_WORKLOAD))}
+    if roof["unit"] == "TFLOP/s":
+        clock[dom_name] = _at_clock(roof["achieved"], _clock_for(dom_name, WORKLOAD))
 
     out = {
         "metric": METRIC,
@@ -332,8 +364,8 @@ def main() -> int:
         "config": {"workload": WORKLOAD, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "pass": "fwd+bwd"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "fwd": {"tflops": round(f_fwd / (per_kernel[0] * 1e-3) / 1e12, 2),
-                "pct_of_peak": round(100 * f_fwd / (per_kernel[0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"tflops": round(fwd_tflops, 2),
+                "pct_of_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
                 "ms": round(per_kernel[0], 4)},
         "fwd_long": {"workload": FWD_WORKLOAD, "ms": round(fwd_long_ms, 4),
                      "tflops": round(fwd_long_tflops, 2),
@@ -341,6 +373,7 @@ def main() -> int:
         "kernels": kernels,
         "event_ms_per_step": round(step_ms, 4),
         "roofline": roof,
+        "clock": clock,
         "csrc_digest": _csrc_digest(),
     }
     if not args.no_per_config:
