@@ -19,6 +19,11 @@ Prints ONE JSON line. Options:
   --no-per-config     skip the forward timings on each named workload (the
                       `forward_per_config` field: median and minimum per
                       launch, roofline fractions, one cold launch at N=4096)
+  --unfused           also time standard attention as separate torch ops
+                      (matmul, mask, softmax, dropout, matmul; the backward
+                      by hand for the backward workload) against the fused
+                      kernels on every workload, with the extra device memory
+                      each allocates (the `unfused_comparison` field)
 """
 from __future__ import annotations
 
@@ -195,12 +200,149 @@ def per_config_forward(attn, W, dev, reuse=None, min_iters=50, min_ms=200.0) -> 
     return out
 
 
+def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) -> dict:
+    """Standard attention as separate torch ops against the fused kernels, on
+    every named workload: S = scale*Q K^T materialised in the input dtype,
+    mask by -inf, softmax, dropout (torch's own RNG: same work, different
+    mask), O = P V; for the backward workload also dV = P^T dO,
+    dP = dO V^T, D = rowsum(dO*O), dS = P*(dP - D), dQ = scale*dS K,
+    dK = scale*dS^T Q. Every right-hand matmul operand is made contiguous
+    first, and those transposed copies are timed separately (the copy share).
+    Reports median times, the device memory each path needs beyond its inputs
+    (outputs, workspace and temporaries), and the largest |O_unfused - O_fused|."""
+    import torch
+    import torch.nn.functional as F
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    def peak_extra(fn):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        fn()
+        torch.cuda.synchronize()
+        return torch.cuda.max_memory_allocated() - base
+
+    out = {}
+    for name, w in W.WORKLOADS.items():
+        inp = W.make_inputs(w)
+        q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+        kv = None if inp.kv_len is None else inp.kv_len.to(dev)
+        do = None if inp.do is None else inp.do.to(dev)
+        seed = W.DROPOUT_SEED if w.dropout_p > 0 else 0
+        reps = reps_large if w.N >= 4096 else reps_small
+        idx = torch.arange(w.N, device=dev)
+        dead = None
+        if w.causal:
+            dead = (idx[None, :] > idx[:, None])[None, None]
+        if kv is not None:
+            pad = (idx[None, :] >= kv[:, None].long())[:, None, None, :]
+            dead = pad if dead is None else (dead | pad)
+        o_f = torch.empty_like(q)
+        lse_f = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        grads_f = tuple(torch.empty_like(q) for _ in range(3)) if do is not None else None
+        ws = None
+        if do is not None:
+            ws = torch.empty(attn.bwd_workspace_bytes(q, causal=w.causal, scale=w.scale),
+                             dtype=torch.uint8, device=dev)
+        state = {}
+
+        def fused():
+            attn.fwd(q, k, v, causal=w.causal, kv_len=kv, dropout_p=w.dropout_p, seed=seed,
+                     scale=w.scale, out=o_f, lse=lse_f)
+            if do is not None:
+                attn.bwd(q, k, v, o_f, lse_f, do, causal=w.causal, kv_len=kv,
+                         dropout_p=w.dropout_p, seed=seed, scale=w.scale, out=grads_f,
+                         workspace=ws)
+
+        def transposes():
+            kt = k.transpose(-1, -2).contiguous()
+            if do is None:
+                return kt, None
+            return kt, v.transpose(-1, -2).contiguous()
+
+        def unfused():
+            kt, vt = transposes()
+            s = torch.matmul(q, kt)
+            s.mul_(w.scale)
+            if dead is not None:
+                s.masked_fill_(dead, float("-inf"))
+            p = torch.softmax(s, dim=-1)
+            del s
+            pd = F.dropout(p, w.dropout_p) if w.dropout_p > 0 else p
+            o = torch.matmul(pd, v)
+            state["o"] = o
+            if do is not None:
+                dv = torch.matmul(pd.transpose(-1, -2).contiguous(), do)
+                dp = torch.matmul(do, vt)
+                dd = (do.float() * o.float()).sum(-1, keepdim=True).to(q.dtype)
+                ds = p * (dp - dd)
+                del dp
+                dq = torch.matmul(ds, k).mul_(w.scale)
+                dk = torch.matmul(ds.transpose(-1, -2).contiguous(), q).mul_(w.scale)
+                state["g"] = (dq, dk, dv)
+
+        def transposes_bwd():
+            # The two N x N transposed copies of the backward, on tensors of
+            # the same shape and dtype as P and dS.
+            t = torch.empty(w.B, w.H, w.N, w.N, dtype=q.dtype, device=dev)
+            t.transpose(-1, -2).contiguous()
+            t.transpose(-1, -2).contiguous()
+
+        t_fused = timed(fused, reps)
+        # The fused path's footprint: its preallocated outputs (and workspace)
+        # plus anything allocated during the call.
+        owned = o_f.nbytes + lse_f.nbytes
+        if do is not None:
+            owned += sum(g.nbytes for g in grads_f) + ws.nbytes
+        m_fused = owned + peak_extra(fused)
+        t_unf = timed(unfused, reps)
+        state.clear()
+        m_unf = peak_extra(unfused)
+        fused()
+        torch.cuda.synchronize()
+        err = float((state["o"].float() - o_f.float()).abs().max().item())
+        state.clear()
+        t_copy = timed(transposes, reps)
+        if do is not None:
+            t_copy += timed(transposes_bwd, reps)
+        flops = w.flops_fwd() + (w.flops_bwd() if do is not None else 0.0)
+        out[name] = {
+            "pass": "fwd+bwd" if do is not None else "fwd",
+            "fused_ms": round(t_fused, 4), "unfused_ms": round(t_unf, 4),
+            "unfused_transposed_copies_ms": round(t_copy, 4),
+            "speedup": round(t_unf / t_fused, 2),
+            "speedup_without_copies": round((t_unf - t_copy) / t_fused, 2),
+            "fused_tflops": round(flops / (t_fused * 1e-3) / 1e12, 1),
+            "fused_bytes": int(m_fused), "unfused_bytes": int(m_unf),
+            "memory_ratio": round(m_unf / m_fused, 1),
+            "max_abs_o_diff": round(err, 5) if w.dropout_p == 0 else None,
+        }
+        del q, k, v, do, kv, o_f, lse_f, grads_f, ws, dead
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="add the unfused torch comparison on every workload")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip timing the forward on each named workload")
     ap.add_argument("--fwd-only", action="store_true",
@@ -379,6 +521,8 @@ def main() -> int:
     if not args.no_per_config:
         out["forward_per_config"] = per_config_forward(
             attn, W, dev, reuse={WORKLOAD: (q, k, v, None)})
+    if args.unfused:
+        out["unfused_comparison"] = unfused_comparison(attn, W, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs)
     print(json.dumps(out))
