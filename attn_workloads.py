@@ -115,14 +115,18 @@ def make_inputs(w: Workload, *, seed: Optional[int] = None) -> Inputs:
 
 def random_case(B: int, H: int, N: int, d: int, dtype: str, *, seed: int,
                 std: float = 1.0, with_do: bool = False,
-                kv_len: Optional[list] = None) -> Inputs:
-    """Small seeded case for sweeps: same recipe as the named workloads."""
+                kv_len: Optional[list] = None, n_k: Optional[int] = None) -> Inputs:
+    """Small seeded case for sweeps: same recipe as the named workloads.
+
+    n_k: number of key/value rows (default N); Q and dO keep N rows.
+    """
     g = torch.Generator().manual_seed(seed)
     shape = (B, H, N, d)
+    kshape = (B, H, N if n_k is None else n_k, d)
     dt = DTYPES[dtype]
     q = (torch.randn(shape, generator=g) * std).to(dt)
-    k = (torch.randn(shape, generator=g) * std).to(dt)
-    v = torch.randn(shape, generator=g).to(dt)
+    k = (torch.randn(kshape, generator=g) * std).to(dt)
+    v = torch.randn(kshape, generator=g).to(dt)
     do = torch.randn(shape, generator=g).to(dt) if with_do else None
     kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32)
     return Inputs(q, k, v, do, kl, 0x9E3779B97F4A7C15 ^ seed)
