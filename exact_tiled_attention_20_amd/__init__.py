@@ -8,11 +8,14 @@ computation runs in the library's HIP kernels; there is no fallback path, and
 the module raises if the library is missing or a call fails.
 
     o, lse = fwd(q, k, v, causal=False, kv_len=None, dropout_p=0.0, seed=0,
-                 scale=None, out_dtype=None)
+                 scale=None, out_dtype=None, window=None)
     dq, dk, dv = bwd(q, k, v, o, lse, do, <same keyword arguments>)
-    keep = dropout_mask(B, H, N, dropout_p, seed, device)
+    keep = dropout_mask(B, H, N, dropout_p, seed, device, n_k=None)
 
-Tensors are (B, H, N, d), contiguous, float16 or bfloat16, d in {64, 128}.
+q and dO are (B, H, N, d); k and v are (B, H, Nk, d) (Nk = N for
+self-attention), contiguous, float16 or bfloat16, d in {64, 128}. Query i
+lines up with key i + Nk - N. window = (left, right) keeps keys at most `left`
+before and `right` after that key (-1: unbounded side).
 """
 from __future__ import annotations
 
@@ -45,6 +48,8 @@ class AttnParams(ctypes.Structure):
         ("kv_len", ctypes.c_void_p),
         ("dropout_p", ctypes.c_float),
         ("seed", ctypes.c_uint64),
+        ("Nk", ctypes.c_int32),
+        ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
     ]
 
 
@@ -94,11 +99,13 @@ def status_string(status: int) -> str:
 
 def make_params(B: int, H: int, N: int, d: int, *, dtype: int, out_dtype: int,
                 scale: float, causal: bool = False, kv_len_ptr: int = 0,
-                dropout_p: float = 0.0, seed: int = 0) -> AttnParams:
+                dropout_p: float = 0.0, seed: int = 0, n_k: int = 0,
+                window=None) -> AttnParams:
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
     return AttnParams(int(B), int(H), int(N), int(d), int(dtype), int(out_dtype),
                       float(scale), 1 if causal else 0,
                       ctypes.c_void_p(kv_len_ptr or None), float(dropout_p),
-                      int(seed) & 0xFFFFFFFFFFFFFFFF)
+                      int(seed) & 0xFFFFFFFFFFFFFFFF, int(n_k), wl, wr)
 
 
 # --------------------------------------------------------------------------
@@ -132,15 +139,15 @@ def _check_qkv(q, k, v):
             raise ValueError(f"{name} must be a device tensor")
         if t.dim() != 4 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous (B, H, N, d) tensor")
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError("q, k, v must have the same shape")
+    if not (k.shape == v.shape and q.shape[:2] == k.shape[:2] and q.shape[3] == k.shape[3]):
+        raise ValueError("q must be (B, H, N, d) and k, v (B, H, Nk, d)")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must have the same dtype")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
 
 
-def _params_from(q, *, causal, kv_len, dropout_p, seed, scale, out_dtype):
+def _params_from(q, k, *, causal, kv_len, dropout_p, seed, scale, out_dtype, window):
     torch = _torch()
     B, H, N, d = q.shape
     if scale is None:
@@ -152,20 +159,23 @@ def _params_from(q, *, causal, kv_len, dropout_p, seed, scale, out_dtype):
                 or not kv_len.is_contiguous():
             raise ValueError("kv_len must be a contiguous int32 device tensor of B entries")
         kv_ptr = kv_len.data_ptr()
+    if window is not None and (len(window) != 2 or min(int(w) for w in window) < -1):
+        raise ValueError("window must be (left, right) with each side >= -1")
     p = make_params(B, H, N, d, dtype=_code(q.dtype), out_dtype=_code(odt), scale=scale,
-                    causal=causal, kv_len_ptr=kv_ptr, dropout_p=dropout_p, seed=seed)
+                    causal=causal, kv_len_ptr=kv_ptr, dropout_p=dropout_p, seed=seed,
+                    n_k=k.shape[2], window=window)
     return p, odt
 
 
 def fwd(q, k, v, *, causal: bool = False, kv_len=None, dropout_p: float = 0.0,
-        seed: int = 0, scale: Optional[float] = None, out_dtype=None,
+        seed: int = 0, scale: Optional[float] = None, out_dtype=None, window=None,
         out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Fused forward: returns (O, lse). O has out_dtype (default q.dtype)."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
-    p, odt = _params_from(q, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
-                          scale=scale, out_dtype=out_dtype)
+    p, odt = _params_from(q, k, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
+                          scale=scale, out_dtype=out_dtype, window=window)
     B, H, N, d = q.shape
     if out is None:
         out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
@@ -179,14 +189,15 @@ def fwd(q, k, v, *, causal: bool = False, kv_len=None, dropout_p: float = 0.0,
 
 
 def bwd_workspace_bytes(q, *, causal=False, kv_len=None, dropout_p=0.0, seed=0,
-                        scale=None, out_dtype=None) -> int:
-    p, _ = _params_from(q, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
-                        scale=scale, out_dtype=out_dtype)
+                        scale=None, out_dtype=None, window=None, k=None) -> int:
+    p, _ = _params_from(q, q if k is None else k, causal=causal, kv_len=kv_len,
+                        dropout_p=dropout_p, seed=seed, scale=scale, out_dtype=out_dtype,
+                        window=window)
     return int(load_library().attn_bwd_workspace_bytes(ctypes.byref(p)))
 
 
 def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None, dropout_p: float = 0.0,
-        seed: int = 0, scale: Optional[float] = None, out_dtype=None,
+        seed: int = 0, scale: Optional[float] = None, out_dtype=None, window=None,
         workspace=None, out=None, stage: Optional[int] = None):
     """Fused backward with recomputation: returns (dQ, dK, dV) in out_dtype.
 
@@ -198,8 +209,8 @@ def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None, dropout_p: fl
     _check_qkv(q, k, v)
     if do.shape != q.shape or do.dtype != q.dtype or not do.is_contiguous():
         raise ValueError("do must match q in shape and dtype and be contiguous")
-    p, odt = _params_from(q, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
-                          scale=scale, out_dtype=out_dtype)
+    p, odt = _params_from(q, k, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
+                          scale=scale, out_dtype=out_dtype, window=window)
     if o.dtype != odt or o.shape != q.shape or not o.is_contiguous():
         raise ValueError("o must be the forward output (same out_dtype and shape)")
     if lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous():
@@ -208,11 +219,14 @@ def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None, dropout_p: fl
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
-        out = tuple(torch.empty(q.shape, dtype=odt, device=q.device) for _ in range(3))
+        out = (torch.empty(q.shape, dtype=odt, device=q.device),
+               torch.empty(k.shape, dtype=odt, device=q.device),
+               torch.empty(k.shape, dtype=odt, device=q.device))
     dq, dk, dv = out
-    for t in out:
-        if t.dtype != odt or t.shape != q.shape or not t.is_contiguous():
-            raise ValueError("gradient outputs must be contiguous, shaped like q, in out_dtype")
+    for t, like in zip(out, (q, k, v)):
+        if t.dtype != odt or t.shape != like.shape or not t.is_contiguous():
+            raise ValueError("gradient outputs must be contiguous, shaped like q, k, v, "
+                             "in out_dtype")
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -227,13 +241,14 @@ def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None, dropout_p: fl
 
 
 def dropout_mask(B: int, H: int, N: int, dropout_p: float, seed: int, device,
-                 d: int = 64) -> "torch.Tensor":
-    """The raw Philox keep decisions, uint8 (B, H, N, N), as the kernels draw them."""
+                 d: int = 64, n_k: Optional[int] = None) -> "torch.Tensor":
+    """The raw Philox keep decisions, uint8 (B, H, N, Nk), as the kernels draw them."""
     torch = _torch()
     lib = load_library()
-    keep = torch.empty((B, H, N, N), dtype=torch.uint8, device=device)
+    nk = N if n_k is None else int(n_k)
+    keep = torch.empty((B, H, N, nk), dtype=torch.uint8, device=device)
     p = make_params(B, H, N, d, dtype=ATTN_F16, out_dtype=ATTN_F16, scale=1.0,
-                    dropout_p=dropout_p, seed=seed)
+                    dropout_p=dropout_p, seed=seed, n_k=nk)
     st = lib.attn_dropout_mask(ctypes.byref(p), keep.data_ptr(), _stream_ptr(device))
     if st != 0:
         raise AttnError(st, "attn_dropout_mask")

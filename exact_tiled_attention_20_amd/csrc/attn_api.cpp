@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 100;  // 0.1.0
+constexpr int32_t kVersion = 200;  // 0.2.0: Nk and the sliding window
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -34,10 +34,14 @@ Range range_of(const void* p, size_t bytes) {
 
 bool overlap(Range x, Range y) { return x.lo < y.hi && y.lo < x.hi; }
 
+// Rows of K and V (0 in the struct means the square case).
+int32_t key_rows(const attn_params* p) { return p->Nk == 0 ? p->N : p->Nk; }
+
 // Shape/dtype/scalar checks common to every entry point.
 attn_status check_params(const attn_params* p) {
   if (p == nullptr) return ATTN_ERR_INVALID_ARG;
   if (p->B < 1 || p->H < 1 || p->N < 1 || p->d < 1) return ATTN_ERR_INVALID_ARG;
+  if (p->Nk < 0 || p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
   if (p->dtype != ATTN_F16 && p->dtype != ATTN_BF16 && p->dtype != ATTN_F32)
     return ATTN_ERR_INVALID_ARG;
   if (p->out_dtype != ATTN_F16 && p->out_dtype != ATTN_BF16 && p->out_dtype != ATTN_F32)
@@ -47,13 +51,16 @@ attn_status check_params(const attn_params* p) {
   if (!(p->dropout_p >= 0.0f && p->dropout_p < 1.0f)) return ATTN_ERR_INVALID_ARG;
   // Element counts: per head N*d must index in 32 bits; the whole tensor must
   // stay far from overflow of 64-bit byte offsets; the grids must fit.
-  const long long per_head = (long long)p->N * p->d;
+  const long long rows = p->N > key_rows(p) ? p->N : key_rows(p);
+  const long long per_head = rows * p->d;
   if (per_head >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   const long long heads = (long long)p->B * p->H;
   if (heads >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   if ((double)heads * (double)per_head >= 4.0e18) return ATTN_ERR_INVALID_ARG;
   const long long blocks = heads * ((p->N + attn::kFwdBlockQ - 1) / attn::kFwdBlockQ);
   if (blocks + 8 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  const long long key_blocks = heads * ((key_rows(p) + 255) / 256);
+  if (key_blocks + 8 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   // Supported kernels.
   if (p->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (p->out_dtype != p->dtype && p->out_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
@@ -68,6 +75,35 @@ uint32_t drop_threshold(float p) {
 
 size_t tensor_bytes(const attn_params* p, int32_t dt) {
   return (size_t)p->B * p->H * p->N * p->d * elem_bytes(dt);
+}
+
+// K, V, dK, dV: (B, H, Nk, d).
+size_t key_tensor_bytes(const attn_params* p, int32_t dt) {
+  return (size_t)p->B * p->H * key_rows(p) * p->d * elem_bytes(dt);
+}
+
+// The key band [i + lo, i + hi] of query row i that the causal mask and the
+// sliding window leave (query i lines up with key i + Nk - N), and the kernel
+// mask mode that applies it: kMaskNone when neither mask is set (every key
+// below the padding length is visible), kMaskCausal for the plain causal band
+// (lo unbounded, hi = 0), kMaskBand otherwise.
+int key_band(const attn_params* p, int* lo, int* hi) {
+  const long long off = (long long)key_rows(p) - p->N;
+  long long l = -attn::kBandInf, h = attn::kBandInf;
+  if (p->causal) h = off;
+  if (p->window_right >= 0 && off + p->window_right < h) h = off + p->window_right;
+  if (p->window_left >= 0) l = off - p->window_left;
+  // Beyond +-kBandInf a bound excludes or admits every key of any valid shape
+  // alike (|i|, |j| < 2^25 since N*d < 2^31), so clamping changes nothing.
+  if (l < -attn::kBandInf) l = -attn::kBandInf;
+  if (h > attn::kBandInf) h = attn::kBandInf;
+  if (h < -attn::kBandInf) h = -attn::kBandInf;
+  if (l > attn::kBandInf) l = attn::kBandInf;
+  *lo = (int)l;
+  *hi = (int)h;
+  if (!(p->causal || p->window_left >= 0 || p->window_right >= 0)) return attn::kMaskNone;
+  if (l == -attn::kBandInf && h == 0) return attn::kMaskCausal;
+  return attn::kMaskBand;
 }
 
 size_t stat_bytes(const attn_params* p) { return (size_t)p->B * p->H * p->N * sizeof(float); }
@@ -97,8 +133,9 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   for (const void* x : ptrs)
     if (x == nullptr || !aligned16(x)) return ATTN_ERR_INVALID_ARG;
   const size_t in_b = tensor_bytes(p, p->dtype);
+  const size_t kin_b = key_tensor_bytes(p, p->dtype);
   const Range outs[] = {range_of(o, tensor_bytes(p, p->out_dtype)), range_of(lse, stat_bytes(p))};
-  const Range ins[] = {range_of(q, in_b), range_of(k, in_b), range_of(v, in_b)};
+  const Range ins[] = {range_of(q, in_b), range_of(k, kin_b), range_of(v, kin_b)};
   if (overlap(outs[0], outs[1])) return ATTN_ERR_INVALID_ARG;
   for (const Range& r : outs)
     for (const Range& x : ins)
@@ -116,6 +153,8 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   a.B = p->B;
   a.H = p->H;
   a.N = p->N;
+  a.Nk = key_rows(p);
+  const int mask = key_band(p, &a.band_lo, &a.band_hi);
   a.nqb = (p->N + attn::kFwdBlockQ - 1) / attn::kFwdBlockQ;
   a.total = p->B * p->H * a.nqb;
   a.per_xcd = (a.total + 7) / 8;
@@ -127,7 +166,7 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   a.drop_rescale = 1.0f / (1.0f - p->dropout_p);
   a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
   a.seed_hi = (uint32_t)(p->seed >> 32);
-  const hipError_t e = attn::launch_fwd(p->dtype == ATTN_BF16 ? 1 : 0, p->d, p->causal != 0,
+  const hipError_t e = attn::launch_fwd(p->dtype == ATTN_BF16 ? 1 : 0, p->d, mask,
                                         dropout, p->out_dtype == ATTN_F32, a,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -158,9 +197,11 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
     return ATTN_ERR_WORKSPACE;
   const size_t in_b = tensor_bytes(p, p->dtype);
   const size_t out_b = tensor_bytes(p, p->out_dtype);
-  const Range outs[] = {range_of(dq, out_b), range_of(dk, out_b), range_of(dv, out_b),
+  const size_t kin_b = key_tensor_bytes(p, p->dtype);
+  const size_t kout_b = key_tensor_bytes(p, p->out_dtype);
+  const Range outs[] = {range_of(dq, out_b), range_of(dk, kout_b), range_of(dv, kout_b),
                         range_of(workspace, need)};
-  const Range ins[] = {range_of(q, in_b), range_of(k, in_b), range_of(v, in_b),
+  const Range ins[] = {range_of(q, in_b), range_of(k, kin_b), range_of(v, kin_b),
                        range_of(o, out_b), range_of(lse, stat_bytes(p)), range_of(d_o, in_b)};
   for (int i = 0; i < 4; ++i) {
     for (int j = i + 1; j < 4; ++j)
@@ -186,6 +227,8 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
   a.B = p->B;
   a.H = p->H;
   a.N = p->N;
+  a.Nk = key_rows(p);
+  const int mask = key_band(p, &a.band_lo, &a.band_hi);
   a.scale = p->scale;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
   const bool dropout = p->dropout_p > 0.0f;
@@ -193,7 +236,7 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
   a.drop_rescale = 1.0f / (1.0f - p->dropout_p);
   a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
   a.seed_hi = (uint32_t)(p->seed >> 32);
-  const hipError_t e = attn::launch_bwd(p->dtype == ATTN_BF16 ? 1 : 0, p->d, p->causal != 0,
+  const hipError_t e = attn::launch_bwd(p->dtype == ATTN_BF16 ? 1 : 0, p->d, mask,
                                         dropout, p->out_dtype == ATTN_F32, stage, a,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -217,17 +260,18 @@ attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream)
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
   if (keep == nullptr || !aligned16(keep)) return ATTN_ERR_INVALID_ARG;
-  const double cells = (double)p->B * p->H * p->N * (double)p->N;
+  const double cells = (double)p->B * p->H * p->N * (double)key_rows(p);
   if (cells >= 9.0e15) return ATTN_ERR_INVALID_ARG;
   attn::MaskArgs a;
   a.keep = keep;
   a.B = p->B;
   a.H = p->H;
   a.N = p->N;
+  a.Nk = key_rows(p);
   a.drop_threshold = drop_threshold(p->dropout_p);
   a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
   a.seed_hi = (uint32_t)(p->seed >> 32);
-  const long long groups = (long long)p->B * p->H * p->N * ((p->N + 3) / 4);
+  const long long groups = (long long)p->B * p->H * p->N * ((key_rows(p) + 3) / 4);
   if ((groups + 255) / 256 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   const hipError_t e = attn::launch_dropout_mask(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

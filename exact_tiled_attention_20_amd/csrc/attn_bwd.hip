@@ -22,6 +22,10 @@
 //   3. dQ: one workgroup per 128 queries (4 waves x 32 queries), the forward's
 //      orientation (S^T = K Q^T, one query per lane) plus dP^T = V dO^T; dQ^T =
 //      K^T dS^T reads K transposed from LDS. Deterministic: no atomics.
+// Banded masks (causal, sliding window, non-square alignment) arrive as the key
+// band [i + band_lo, i + band_hi] of query row i, as in the forward: the dK/dV
+// kernel visits only the query tiles whose rows see one of its keys, the dQ
+// kernel only the key tiles its rows see.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs 
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = 64 * kDkdvWaves;
 
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
+template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int NW = kDkdvWaves;
@@ -89,6 +93,8 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int TILE_BYTES = BQ * D * 2;
   constexpr int KV_BYTES = BKW * D * 2;
   constexpr int QW = (TILE_BYTES / 1024 < NW) ? TILE_BYTES / 1024 : NW;  // waves that load a tile
+  constexpr bool BAND = MASK != kMaskNone;
+  constexpr bool LO = MASK == kMaskBand;   // a lower band edge exists
 
   // LDS: the Q and dO tiles first (within reach of the 16-bit immediate
   // offset of LDS reads), then one block per wave holding that wave's 32 K
@@ -100,7 +106,7 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   char* const ob0 = smem + 2 * TILE_BYTES;       // [2] dO tiles
   constexpr int KVB = 4 * TILE_BYTES;            // byte offset of the per-wave K/V blocks
 
-  const int nkb = (a.N + BKW - 1) / BKW;
+  const int nkb = (a.Nk + BKW - 1) / BKW;
   const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, nkb);
   if (!wi.valid) return;
   const int bh = wi.bh;
@@ -109,9 +115,10 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   const int h = bh - b * a.H;
   const int N = a.N;
   const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t khead = (size_t)bh * (size_t)a.Nk * D;
   const uint16_t* __restrict__ Q = a.q + head;
-  const uint16_t* __restrict__ K = a.k + head;
-  const uint16_t* __restrict__ V = a.v + head;
+  const uint16_t* __restrict__ K = a.k + khead;
+  const uint16_t* __restrict__ V = a.v + khead;
   const uint16_t* __restrict__ dO = a.d_o + head;
   const float* __restrict__ LSE = a.lse2 + (size_t)bh * N;  // lse * log2(e)
   const float* __restrict__ DEL = a.delta + (size_t)bh * N;
@@ -125,8 +132,10 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   const int kw = k0 + 32 * w;
   const int j = kw + l32;              // this lane's key
 
-  int kv_end = N;
-  if (a.kv_len != nullptr) kv_end = min(max(a.kv_len[b], 0), N);
+  int kv_end = a.Nk;
+  if (a.kv_len != nullptr) kv_end = min(max(a.kv_len[b], 0), a.Nk);
+  const int band_lo = LO ? a.band_lo : -kBandInf;
+  const int band_hi = MASK == kMaskCausal ? 0 : a.band_hi;
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -140,8 +149,19 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   if (k0 < kv_end) {
     const bool key_tail = kw + 32 > kv_end;
     const bool wave_has_keys = kw < kv_end;
-    const int qt0 = CAUSAL ? (k0 / BQ) : 0;
-    const int nqt = (N + BQ - 1) / BQ;
+    // Query tiles [qt0, nqt) hold every row that sees one of this block's
+    // keys: row i sees key j only if j - band_hi <= i <= j - band_lo.
+    int qt0 = 0;
+    int nqt = (N + BQ - 1) / BQ;
+    if (BAND) {
+      // Rounded down to an even tile (one extra, fully skipped tile at most):
+      // with an even start the loop unrolled by two fits the register budget.
+      qt0 = MASK == kMaskCausal ? k0 / BQ : (max(0, k0 - band_hi) / BQ) & ~1;
+      if (LO) {
+        const int last_row = k0 + BKW - 1 - band_lo;
+        nqt = last_row < 0 ? 0 : min(nqt, last_row / BQ + 1);
+      }
+    }
     {
       // Wave w's slices of the 256-row K/V block are exactly its own 32 keys.
       TilePairLoader<D, BKW, NW> kvload;
@@ -183,7 +203,9 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
       __syncthreads();
       if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
       const int qbase = t * BQ;
-      const bool active = wave_has_keys && (!CAUSAL || qbase + 31 >= kw);
+      const bool active = wave_has_keys &&
+                          (!BAND || (qbase + 31 >= kw - band_hi &&
+                                     (!LO || qbase <= kw + 31 - band_lo)));
       if (!active) return;
       const char* qb = qb0 + buf * TILE_BYTES;
       const char* ob = ob0 + buf * TILE_BYTES;
@@ -225,7 +247,9 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
 
       // P (masked), dropout, dS; packed as MFMA A operands for 16-query steps.
       // Register r holds query qbase + 8(r/4) + 4hh + r%4.
-      const bool need_mask = (CAUSAL && qbase < kw + 31) || key_tail || (qbase + 32 > N);
+      const bool need_mask =
+          (BAND && (qbase + band_hi < kw + 31 || (LO && qbase + 31 + band_lo > kw))) || key_tail ||
+          (qbase + 32 > N);
       auto grad = [&](u32x4 (&pa)[2], u32x4 (&sa)[2], auto masked) {
         f32x16 pz, ds;
 #pragma unroll
@@ -236,7 +260,8 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
             const int qi = qbase + 8 * g4 + 4 * hh + e;
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[g4][e]));
             if (decltype(masked)::value) {
-              const bool dead = (CAUSAL & (j > qi)) | (j >= kv_end) | (qi >= N);
+              const bool dead = (BAND & ((j > qi + band_hi) | (LO & (j < qi + band_lo)))) |
+                                (j >= kv_end) | (qi >= N);
               p = dead ? 0.f : p;
             }
             float z = 1.f;
@@ -290,8 +315,8 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kw + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (key < N) {
-        const size_t idx = head + (size_t)key * D + 32 * db + l32;
+      if (key < a.Nk) {
+        const size_t idx = khead + (size_t)key * D + 32 * db + l32;
         const float gk = dk[db][r] * a.scale;
         const float gv = dv[db][r];
         if (OUT_F32) {
@@ -312,7 +337,7 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
 // B operand of dQ^T += K^T dS^T (K read transposed from LDS). K/V tiles of 64
 // keys are copied HBM -> LDS directly; each tile is processed as two 32-key
 // halves to keep two waves per SIMD.
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
+template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(const BwdArgs a) {
   constexpr int BR = 128;
@@ -320,6 +345,8 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   constexpr int KK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TILE_BYTES = BC * D * 2;
+  constexpr bool BAND = MASK != kMaskNone;
+  constexpr bool LO = MASK == kMaskBand;   // a lower band edge exists
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
 
@@ -327,15 +354,16 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, nqb);
   if (!wi.valid) return;
   const int bh = wi.bh;
-  const int qblk = CAUSAL ? nqb - 1 - wi.rank : wi.rank;  // heaviest first
+  const int qblk = BAND ? nqb - 1 - wi.rank : wi.rank;  // heaviest first
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int N = a.N;
   const int q0 = qblk * BR;
   const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t khead = (size_t)bh * (size_t)a.Nk * D;
   const uint16_t* __restrict__ Q = a.q + head;
-  const uint16_t* __restrict__ K = a.k + head;
-  const uint16_t* __restrict__ V = a.v + head;
+  const uint16_t* __restrict__ K = a.k + khead;
+  const uint16_t* __restrict__ V = a.v + khead;
   const uint16_t* __restrict__ dO = a.d_o + head;
 
   const int tid = threadIdx.x;
@@ -344,10 +372,17 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  int kv_end = N;
-  if (a.kv_len != nullptr) kv_end = min(max(a.kv_len[b], 0), N);
+  int kv_end = a.Nk;
+  if (a.kv_len != nullptr) kv_end = min(max(a.kv_len[b], 0), a.Nk);
+  const int band_lo = LO ? a.band_lo : -kBandInf;
+  const int band_hi = MASK == kMaskCausal ? 0 : a.band_hi;
+  // Key tiles [t0, ntiles) hold every key a row of this block sees.
   int kend = kv_end;
-  if (CAUSAL) kend = min(kend, q0 + BR);
+  int t0 = 0;
+  if (BAND) {
+    kend = min(kend, max(0, min(q0 + BR, N) + band_hi));
+    if (LO) t0 = max(0, q0 + band_lo) / BC;
+  }
   const int ntiles = (kend + BC - 1) / BC;
 
   const int wq0 = q0 + 32 * w;
@@ -397,7 +432,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   const float c2 = a.scale_log2;
 
-  if (ntiles > 0) loader.issue(K, V, 0, kv_end, kb0, vb0);
+  if (ntiles > t0) loader.issue(K, V, t0 * BC, kv_end, kb0, vb0);
   // The loop body is instantiated once per buffer (the loop is unrolled by
   // two), so every LDS address is a per-lane offset plus a constant that the
   // read instructions carry as their immediate offset.
@@ -412,11 +447,15 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
       loader.issue_one_untracked(V, (t + 1) * BC, kv_end, vb0 + (buf ^ 1) * TILE_BYTES);
     }
     const int k0 = t * BC;
-    const bool active = wave_has_rows && (!CAUSAL || k0 <= wq0 + 31);
+    const bool active = wave_has_rows &&
+                        (!BAND || (k0 <= wq0 + 31 + band_hi &&
+                                   (!LO || k0 + BC - 1 >= wq0 + band_lo)));
     if (!active) return;
     const char* kb = kb0 + buf * TILE_BYTES;
     const char* vb = vb0 + buf * TILE_BYTES;
-    const bool need_mask = (CAUSAL && (k0 + BC - 1 > wq0)) || (k0 + BC > kv_end);
+    const bool need_mask =
+        (BAND && (k0 + BC - 1 > wq0 + band_hi || (LO && k0 < wq0 + 31 + band_lo))) ||
+        (k0 + BC > kv_end);
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       // S^T and dP^T for keys k0 + 32 kb2 .. +32 (lane = query).
@@ -451,7 +490,8 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
             if (decltype(masked)::value) {
               const int jj = j0 + e;
-              p = ((CAUSAL && jj > qi) || jj >= kv_end) ? 0.f : p;
+              p = ((BAND && (jj > qi + band_hi || (LO && jj < qi + band_lo))) || jj >= kv_end)
+                      ? 0.f : p;
             }
             float dpz = dp[r];
             if (DROPOUT) dpz = (u[e] >= a.drop_threshold) ? dpz * a.drop_rescale : 0.f;
@@ -479,7 +519,8 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
       }
     }
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  // Buffers are counted from t0: tile t lives in buffer (t - t0) & 1.
+  for (int t = t0; t < ntiles; t += 2) {
     tile_step(t, std::integral_constant<int, 0>());
     if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
   }
@@ -504,7 +545,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   }
 }
 
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
+template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (stage < 0 || stage == 0) {
@@ -516,9 +557,9 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 1) {
-    const int nkb = (a.N + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
+    const int nkb = (a.Nk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
     const int tk = a.B * a.H * nkb;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>),
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<E, D, MASK, DROPOUT, OUT_F32>),
                        dim3(((tk + 7) / 8) * 8), dim3(kDkdvThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -526,36 +567,37 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
   if (stage < 0 || stage == 2) {
     const int nqb = (a.N + 127) / 128;
     const int tq = a.B * a.H * nqb;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>),
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<E, D, MASK, DROPOUT, OUT_F32>),
                        dim3(((tq + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
     e = hipGetLastError();
   }
   return e;
 }
 
-template <typename E, int D>
-static hipError_t launch_d(bool causal, bool dropout, bool out_f32, int st, const BwdArgs& a,
-                           hipStream_t s) {
-  if (causal) {
-    if (dropout) return out_f32 ? launch_all<E, D, true, true, true>(st, a, s)
-                                : launch_all<E, D, true, true, false>(st, a, s);
-    return out_f32 ? launch_all<E, D, true, false, true>(st, a, s)
-                   : launch_all<E, D, true, false, false>(st, a, s);
-  }
-  if (dropout) return out_f32 ? launch_all<E, D, false, true, true>(st, a, s)
-                              : launch_all<E, D, false, true, false>(st, a, s);
-  return out_f32 ? launch_all<E, D, false, false, true>(st, a, s)
-                 : launch_all<E, D, false, false, false>(st, a, s);
+template <typename E, int D, int MASK>
+static hipError_t launch_m(bool dropout, bool out_f32, int st, const BwdArgs& a, hipStream_t s) {
+  if (dropout) return out_f32 ? launch_all<E, D, MASK, true, true>(st, a, s)
+                              : launch_all<E, D, MASK, true, false>(st, a, s);
+  return out_f32 ? launch_all<E, D, MASK, false, true>(st, a, s)
+                 : launch_all<E, D, MASK, false, false>(st, a, s);
 }
 
-hipError_t launch_bwd(int dtype, int d, bool causal, bool dropout, bool out_f32, int stage,
+template <typename E, int D>
+static hipError_t launch_d(int mask, bool dropout, bool out_f32, int st, const BwdArgs& a,
+                           hipStream_t s) {
+  if (mask == kMaskCausal) return launch_m<E, D, kMaskCausal>(dropout, out_f32, st, a, s);
+  if (mask == kMaskBand) return launch_m<E, D, kMaskBand>(dropout, out_f32, st, a, s);
+  return launch_m<E, D, kMaskNone>(dropout, out_f32, st, a, s);
+}
+
+hipError_t launch_bwd(int dtype, int d, int mask, bool dropout, bool out_f32, int stage,
                       const BwdArgs& a, hipStream_t stream) {
   if (dtype == 1) {
-    if (d == 128) return launch_d<Elem<bf16_t>, 128>(causal, dropout, out_f32, stage, a, stream);
-    return launch_d<Elem<bf16_t>, 64>(causal, dropout, out_f32, stage, a, stream);
+    if (d == 128) return launch_d<Elem<bf16_t>, 128>(mask, dropout, out_f32, stage, a, stream);
+    return launch_d<Elem<bf16_t>, 64>(mask, dropout, out_f32, stage, a, stream);
   }
-  if (d == 128) return launch_d<Elem<f16_t>, 128>(causal, dropout, out_f32, stage, a, stream);
-  return launch_d<Elem<f16_t>, 64>(causal, dropout, out_f32, stage, a, stream);
+  if (d == 128) return launch_d<Elem<f16_t>, 128>(mask, dropout, out_f32, stage, a, stream);
+  return launch_d<Elem<f16_t>, 64>(mask, dropout, out_f32, stage, a, stream);
 }
 
 }  // namespace attn

@@ -29,6 +29,11 @@
 //     same XCD (workgroup ids are dispatched round-robin over the 8 XCDs), which
 //     keeps that head's K/V re-reads in one L2; under a causal mask the
 //     heaviest (last) query blocks of all of an XCD's heads start first.
+//   * Banded masks -- causal, sliding window, and the bottom-right alignment of
+//     a non-square Q x K grid (the variants named in the page's section "When
+//     it falls down") -- arrive as one key band [i + band_lo, i + band_hi] per
+//     query row i. A workgroup visits only the K/V tiles that meet the band of
+//     one of its rows; tiles that cross a band edge are masked element-wise.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -36,7 +41,7 @@
 
 namespace attn {
 
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
+template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const FwdArgs a) {
   constexpr int BR = kFwdBlockQ;
@@ -46,21 +51,24 @@ void attn_fwd_kernel(const FwdArgs a) {
   constexpr int NKB = BC / 32;          // 32-key blocks of S^T per tile
   constexpr int NC16 = BC / 16;         // 16-key MFMA steps of the PV product
   constexpr int TILE_BYTES = BC * D * 2;
+  constexpr bool BAND = MASK != kMaskNone;
+  constexpr bool LO = MASK == kMaskBand;   // a lower band edge exists
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
 
   const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, a.nqb);
   if (!wi.valid) return;
   const int bh = wi.bh;
-  const int qb = CAUSAL ? a.nqb - 1 - wi.rank : wi.rank;  // heaviest first
+  const int qb = BAND ? a.nqb - 1 - wi.rank : wi.rank;  // heaviest first
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int N = a.N;
   const int q0 = qb * BR;
   const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t khead = (size_t)bh * (size_t)a.Nk * D;
   const uint16_t* __restrict__ Q = a.q + head;
-  const uint16_t* __restrict__ K = a.k + head;
-  const uint16_t* __restrict__ V = a.v + head;
+  const uint16_t* __restrict__ K = a.k + khead;
+  const uint16_t* __restrict__ V = a.v + khead;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,10 +76,18 @@ void attn_fwd_kernel(const FwdArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  int kv_end = N;
-  if (a.kv_len != nullptr) kv_end = min(max(a.kv_len[b], 0), N);
+  int kv_end = a.Nk;
+  if (a.kv_len != nullptr) kv_end = min(max(a.kv_len[b], 0), a.Nk);
+  const int band_lo = LO ? a.band_lo : -kBandInf;
+  const int band_hi = MASK == kMaskCausal ? 0 : a.band_hi;
+  // Tiles [t0, ntiles) hold every key visible to a row of this block: from the
+  // first row's lower band edge to the last row's upper band edge.
   int kend = kv_end;
-  if (CAUSAL) kend = min(kend, q0 + BR);
+  int t0 = 0;
+  if (BAND) {
+    kend = min(kend, max(0, min(q0 + BR, N) + band_hi));
+    if (LO) t0 = max(0, q0 + band_lo) / BC;
+  }
   const int ntiles = (kend + BC - 1) / BC;
 
   const int wq0 = q0 + w * 32;          // first query row of this wave
@@ -132,10 +148,15 @@ void attn_fwd_kernel(const FwdArgs a) {
   const float c2 = a.scale_log2;
   const float thr = a.rescale_thr;
 
-  // Tiles this wave computes: under a causal mask a wave stops at the tile
-  // holding its last row's diagonal (it keeps meeting the barriers).
+  // Tiles this wave computes: under a band a wave stops after the tile that
+  // holds its last row's upper band edge (it keeps meeting the barriers).
+  // Every wave starts at the block's first tile; keys below a wave's own
+  // lower band edge are masked.
   int ntiles_w = wave_has_rows ? ntiles : 0;
-  if (CAUSAL) ntiles_w = min(ntiles_w, (wq0 + 31) / BC + 1);
+  if (BAND) {
+    const int last_key = wq0 + 31 + band_hi;
+    ntiles_w = last_key < 0 ? 0 : min(ntiles_w, last_key / BC + 1);
+  }
 
   // Scores of one tile: S^T = K Q^T, 32 keys x 32 queries per block. The
   // NKB accumulator chains are interleaved step by step: a single chain of
@@ -154,15 +175,16 @@ void attn_fwd_kernel(const FwdArgs a) {
     }
   };
   auto no_hook = [](int) {};
-  // Mask (causal diagonal tiles, the ragged tail, key padding) of the tile
-  // starting at key k0, and the row maximum of a tile.
+  // Mask (band edges, the ragged tail, key padding) of the tile starting at
+  // key k0, and the row maximum of a tile.
   auto mask = [&](f32x16 (&s)[NKB], int k0) {
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = k0 + kb2 * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool dead = (CAUSAL && j > qi) || (j >= kv_end);
+        const bool dead =
+            (BAND && (j > qi + band_hi || (LO && j < qi + band_lo))) || (j >= kv_end);
         if (dead) s[kb2][r] = -INFINITY;
       }
   };
@@ -175,7 +197,8 @@ void attn_fwd_kernel(const FwdArgs a) {
     return halves_max(mx);
   };
   auto need_mask = [&](int k0) {
-    return (CAUSAL && (k0 + BC - 1 > wq0)) || (k0 + BC > kv_end);
+    return (BAND && (k0 + BC - 1 > wq0 + band_hi || (LO && k0 < wq0 + 31 + band_lo))) ||
+           (k0 + BC > kv_end);
   };
   // Online softmax, lazy form: the reference is raised only when the tile's
   // row maximum exceeds it by more than the threshold.
@@ -193,18 +216,19 @@ void attn_fwd_kernel(const FwdArgs a) {
     }
   };
 
-  // Scores of tile t (raw q.k) live in ss[t & 1]: iteration t reads one set
-  // and fills the other, so no copy is needed between iterations.
+  // Scores of tile t (raw q.k) live in ss[(t - t0) & 1]: iteration t reads
+  // one set and fills the other, so no copy is needed between iterations.
+  // Buffers are counted from the block's first tile t0 the same way.
   f32x16 ss[2][NKB];
-  if (ntiles > 0) {
-    loader.issue_one_untracked(K, 0, kv_end, kb0);
-    loader.issue_one_untracked(V, 0, kv_end, vb0);
+  if (ntiles > t0) {
+    loader.issue_one_untracked(K, t0 * BC, kv_end, kb0);
+    loader.issue_one_untracked(V, t0 * BC, kv_end, vb0);
     wait_all_memory();
     __syncthreads();
-    if (ntiles > 1) loader.issue_one_untracked(K, BC, kv_end, kb0 + TILE_BYTES);
-    if (ntiles_w > 0) {
+    if (t0 + 1 < ntiles) loader.issue_one_untracked(K, (t0 + 1) * BC, kv_end, kb0 + TILE_BYTES);
+    if (ntiles_w > t0) {
       scores(kb0, ss[0], no_hook);
-      if (need_mask(0)) mask(ss[0], 0);
+      if (need_mask(t0 * BC)) mask(ss[0], t0 * BC);
       rescale(row_max(ss[0]));
     }
   }
@@ -212,8 +236,8 @@ void attn_fwd_kernel(const FwdArgs a) {
   // Iteration t: P(t) = exp(S(t) - m) times V(t). The MFMAs of
   // S(t+1) = K(t+1) Q^T run beside the exponentials of tile t, and the row
   // maximum of tile t+1 (with the reference update it triggers) beside the PV
-  // MFMAs. K(t) and V(t) live in buffer t & 1 of their region; K runs one tile
-  // ahead of V. After a wave's last tile the scores of the next one are formed
+  // MFMAs. K(t) and V(t) live in buffer (t - t0) & 1 of their region; K runs
+  // one tile ahead of V. After a wave's last tile the scores of the next one are formed
   // from whatever that buffer holds and discarded, which keeps the body one
   // straight-line block.
   // With SPREAD the copies of K(t+2) and V(t+1) (both full tiles) are issued
@@ -340,12 +364,12 @@ void attn_fwd_kernel(const FwdArgs a) {
   const int tsp = max(0, min(ntiles - 2, kv_end / BC - 2));
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  int t = 0;
+  int t = t0;
   for (; t + 1 < tsp; t += 2) {
     tile_step(t, C0(), std::true_type());
     tile_step(t + 1, C1(), std::true_type());
   }
-  // t is even here.
+  // t - t0 is even here.
   for (; t < ntiles; t += 2) {
     tile_step(t, C0(), std::false_type());
     if (t + 1 < ntiles) tile_step(t + 1, C1(), std::false_type());
@@ -381,37 +405,38 @@ void attn_fwd_kernel(const FwdArgs a) {
   }
 }
 
-template <typename E, int D, bool CAUSAL, bool DROPOUT, bool OUT_F32>
+template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 static hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
   const dim3 grid(a.per_xcd * 8);
-  hipLaunchKernelGGL((attn_fwd_kernel<E, D, CAUSAL, DROPOUT, OUT_F32>), grid,
+  hipLaunchKernelGGL((attn_fwd_kernel<E, D, MASK, DROPOUT, OUT_F32>), grid,
                      dim3(kFwdThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename E, int D>
-static hipError_t launch_d(bool causal, bool dropout, bool out_f32, const FwdArgs& a,
-                           hipStream_t s) {
-  if (causal) {
-    if (dropout) return out_f32 ? launch_one<E, D, true, true, true>(a, s)
-                                : launch_one<E, D, true, true, false>(a, s);
-    return out_f32 ? launch_one<E, D, true, false, true>(a, s)
-                   : launch_one<E, D, true, false, false>(a, s);
-  }
-  if (dropout) return out_f32 ? launch_one<E, D, false, true, true>(a, s)
-                              : launch_one<E, D, false, true, false>(a, s);
-  return out_f32 ? launch_one<E, D, false, false, true>(a, s)
-                 : launch_one<E, D, false, false, false>(a, s);
+template <typename E, int D, int MASK>
+static hipError_t launch_m(bool dropout, bool out_f32, const FwdArgs& a, hipStream_t s) {
+  if (dropout) return out_f32 ? launch_one<E, D, MASK, true, true>(a, s)
+                              : launch_one<E, D, MASK, true, false>(a, s);
+  return out_f32 ? launch_one<E, D, MASK, false, true>(a, s)
+                 : launch_one<E, D, MASK, false, false>(a, s);
 }
 
-hipError_t launch_fwd(int dtype, int d, bool causal, bool dropout, bool out_f32,
+template <typename E, int D>
+static hipError_t launch_d(int mask, bool dropout, bool out_f32, const FwdArgs& a,
+                           hipStream_t s) {
+  if (mask == kMaskCausal) return launch_m<E, D, kMaskCausal>(dropout, out_f32, a, s);
+  if (mask == kMaskBand) return launch_m<E, D, kMaskBand>(dropout, out_f32, a, s);
+  return launch_m<E, D, kMaskNone>(dropout, out_f32, a, s);
+}
+
+hipError_t launch_fwd(int dtype, int d, int mask, bool dropout, bool out_f32,
                       const FwdArgs& a, hipStream_t stream) {
   if (dtype == 1) {
-    if (d == 128) return launch_d<Elem<bf16_t>, 128>(causal, dropout, out_f32, a, stream);
-    return launch_d<Elem<bf16_t>, 64>(causal, dropout, out_f32, a, stream);
+    if (d == 128) return launch_d<Elem<bf16_t>, 128>(mask, dropout, out_f32, a, stream);
+    return launch_d<Elem<bf16_t>, 64>(mask, dropout, out_f32, a, stream);
   }
-  if (d == 128) return launch_d<Elem<f16_t>, 128>(causal, dropout, out_f32, a, stream);
-  return launch_d<Elem<f16_t>, 64>(causal, dropout, out_f32, a, stream);
+  if (d == 128) return launch_d<Elem<f16_t>, 128>(mask, dropout, out_f32, a, stream);
+  return launch_d<Elem<f16_t>, 64>(mask, dropout, out_f32, a, stream);
 }
 
 }  // namespace attn

@@ -27,15 +27,27 @@
  *     it' is carrying" (the result is exact; O(N) extra memory).
  *
  * Conventions shared by every entry point
- *   Layout.  Q, K, V, O, dO, dQ, dK, dV are dense row-major (B, H, N, d)
- *            arrays: element (b, h, i, c) sits at ((b*H + h)*N + i)*d + c.
- *            lse and the backward's D are (B, H, N) float32.
- *   Masks.   causal: key j is visible to query i iff j <= i (square N x N).
+ *   Layout.  Q, O, dO, dQ are dense row-major (B, H, N, d) arrays: element
+ *            (b, h, i, c) sits at ((b*H + h)*N + i)*d + c. K, V, dK, dV are
+ *            (B, H, Nk, d) in the same layout, Nk = N unless set (cross-
+ *            attention with a non-square grid). lse and the backward's D are
+ *            (B, H, N) float32.
+ *   Masks.   Query i lines up with key c_i = i + Nk - N (the last query with
+ *            the last key; c_i = i when Nk = N). Every set mask must keep a
+ *            key for it to be visible:
+ *            causal: j <= c_i.
+ *            sliding window: c_i - window_left <= j <= c_i + window_right,
+ *            each side unbounded when its value is -1 (Mistral-style: causal
+ *            with window_left = w - 1; Longformer-style: both sides w).
  *            key padding: kv_len is a device array of B int32; key j is
- *            visible iff j < kv_len[b] (values are clamped to [0, N]; query
- *            rows at or past kv_len[b] are still computed). Both may be set.
+ *            visible iff j < kv_len[b] (values are clamped to [0, Nk]; query
+ *            rows are all computed).
  *            A query row with no visible key yields O = 0, lse = -inf and
  *            zero gradients.
+ *            ("Why FlashAttention Is a Kernel Story", section "When it falls
+ *            down": sliding-window attention and cross-attention with
+ *            non-square K, V grids are the variants that change the tiling;
+ *            the alignment and the window bounds are this library's reading.)
  *   Dropout. p in [0, 1). Each probability is kept iff the 32-bit draw
  *            u = Philox4x32-10(counter = (j >> 2, i, h, b), key = seed)[j & 3]
  *            satisfies u >= floor(p_f32 * 2^32); kept values are scaled by
@@ -80,8 +92,9 @@ typedef enum {
 typedef struct {
   int32_t B, H, N, d;      /* batch, heads, sequence length, head dim.
                               B, H, N >= 1; d in {64, 128};
-                              B*H*N*d must fit in int32 index math per head
-                              and the total element count below 2^62.      */
+                              N*d and Nk*d must be below 2^31 (per-head
+                              index math) and the element counts of every
+                              tensor below about 2^62.                     */
   int32_t dtype;           /* attn_dtype of Q, K, V, dO: ATTN_F16 or BF16  */
   int32_t out_dtype;       /* attn_dtype of O, dQ, dK, dV: == dtype or F32 */
   float scale;             /* multiplies Q K^T; finite and > 0             */
@@ -89,10 +102,14 @@ typedef struct {
   const int32_t* kv_len;   /* device int32[B] of valid key counts, or NULL */
   float dropout_p;         /* 0 <= p < 1; 0 disables dropout               */
   uint64_t seed;           /* Philox key for dropout                       */
+  int32_t Nk;              /* rows of K, V, dK, dV; 0 means Nk = N; >= 0   */
+  int32_t window_left;     /* sliding window, keys before c_i; -1 = none   */
+  int32_t window_right;    /* sliding window, keys after c_i;  -1 = none   */
 } attn_params;
 
 /* Forward: O (out_dtype, (B,H,N,d)) and lse (float32, (B,H,N)), where
- * lse_i = log sum_j exp(scale * Q_i . K_j) over the visible keys. */
+ * lse_i = log sum_j exp(scale * Q_i . K_j) over the visible keys. K and V are
+ * (B,H,Nk,d). */
 attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
                      const void* v, void* o, float* lse, void* stream);
 
@@ -101,8 +118,8 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
 size_t attn_bwd_workspace_bytes(const attn_params* p);
 
 /* Backward: given Q, K, V, the forward's O (out_dtype) and lse, and dO
- * (dtype), writes dQ, dK, dV (out_dtype). Scores and probabilities are
- * recomputed from lse; nothing N x N is stored. `workspace` is a device
+ * (dtype), writes dQ (B,H,N,d), dK and dV (B,H,Nk,d), all in out_dtype.
+ * Scores and probabilities are recomputed from lse; nothing N x Nk is stored. `workspace` is a device
  * buffer of at least attn_bwd_workspace_bytes(p) bytes, owned by the caller,
  * 256-byte aligned; its contents on entry do not matter. */
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
@@ -132,8 +149,9 @@ attn_status attn_bwd_stage(const attn_params* p, int32_t stage, const void* q,
                            void* stream);
 
 /* Test aid: writes the dropout keep-mask keep[b][h][i][j] (uint8 0/1, device,
- * (B,H,N,N)) that attn_fwd and attn_bwd use for these parameters. Masking by
- * causal/kv_len is not applied here: it is the raw Philox keep decision. */
+ * (B,H,N,Nk)) that attn_fwd and attn_bwd use for these parameters. Masking by
+ * causal/window/kv_len is not applied here: it is the raw Philox keep
+ * decision. */
 attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream);
 
 /* Static, human-readable text for a status code. */

@@ -38,17 +38,20 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_version() == 100
+    assert lib.attn_version() == 200
     for code, name in attn.STATUS_NAMES.items():
         assert attn.status_string(code).startswith(name)
     assert "unknown" in attn.status_string(99)
 
 
 def test_struct_layout_matches_header():
-    # int32 x 6, float, int32, pointer (8-aligned), float, uint64
-    assert ctypes.sizeof(attn.AttnParams) == 56
+    # int32 x 6, float, int32, pointer (8-aligned), float, uint64, int32 x 3
+    assert ctypes.sizeof(attn.AttnParams) == 72
     assert attn.AttnParams.kv_len.offset == 32
     assert attn.AttnParams.seed.offset == 48
+    assert attn.AttnParams.Nk.offset == 56
+    assert attn.AttnParams.window_left.offset == 60
+    assert attn.AttnParams.window_right.offset == 64
 
 
 FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation fails first
@@ -77,7 +80,9 @@ INVALID = [
     dict(scale=0.0), dict(scale=-0.125), dict(scale=float("inf")), dict(scale=float("nan")),
     dict(dropout_p=1.0), dict(dropout_p=-0.1), dict(dropout_p=float("nan")),
     dict(N=1 << 24, d=128),           # N*d per head overflows int32 indexing
+    dict(N=8, n_k=1 << 24, d=128),    # Nk*d per head overflows int32 indexing
     dict(B=1 << 16, H=1 << 15),       # B*H overflows
+    dict(n_k=-1), dict(window=(-2, 0)), dict(window=(0, -7)),
 ]
 UNSUPPORTED = [
     dict(d=96), dict(d=256), dict(d=32),
@@ -183,3 +188,15 @@ def test_dropout_mask_pointer_checks(lib):
     p = _params(dropout_p=0.1)
     assert lib.attn_dropout_mask(ctypes.byref(p), None, None) == 1
     assert lib.attn_dropout_mask(ctypes.byref(p), FAKE + 1, None) == 1
+
+
+def test_aliasing_checks_cover_the_key_rows(lib):
+    """K and V span (B, H, Nk, d): an output placed past their first N rows but
+    inside their Nk rows still aliases them."""
+    p = _params(N=100, n_k=1000)
+    q, k, v, o, lse = _ptrs(5)
+    inside_k = k + 2 * 3 * 100 * 64 * 2 + 4096
+    assert _fwd(lib, p, [q, k, v, inside_k, lse]) == 1
+    ptrs = _ptrs(10)
+    ptrs[7] = ptrs[1] + 2 * 3 * 500 * 64 * 2          # dk inside k's key rows
+    assert _bwd(lib, p, ptrs) == 1
