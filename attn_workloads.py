@@ -14,7 +14,7 @@ the storage dtype, so every consumer sees identical bits.
 from __future__ import annotations
 
 import dataclasses
-from typing import Optional
+from typing import Optional, Tuple
 
 import torch
 
@@ -40,6 +40,12 @@ class Workload:
     qk_std: float = 1.0      # Q and K drawn as qk_std * N(0, 1)
     backward: bool = False   # the workload includes dO and the backward pass
     seed: int = 0
+    n_k: int = 0             # rows of K and V (0: N, self-attention)
+    window: Optional[Tuple[int, int]] = None   # (left, right), -1 unbounded
+
+    @property
+    def Nk(self) -> int:
+        return self.n_k or self.N
 
     @property
     def scale(self) -> float:
@@ -79,6 +85,20 @@ WORKLOADS = {
 # Order matters: the first is the small case, the third is the headline forward.
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# The masked variants the method's description names as needing tiling changes
+# (sliding-window attention, cross-attention on a non-square grid), at the
+# sizes of the 16K-context layer: a Mistral-style causal window of 4096 keys,
+# and a 2048-query chunk attending causally (bottom-right) to a 16384-key
+# context, as in chunked prefill against a key/value cache.
+VARIANTS = {
+    "swa4096_b1h32n16384d128_bf16_bwd": Workload(
+        "swa4096_b1h32n16384d128_bf16_bwd", B=1, H=32, N=16384, d=128, dtype="bf16",
+        causal=True, window=(4095, -1), backward=True, seed=1006),
+    "chunk_b4h16n2048nk16384d128_bf16_causal_bwd": Workload(
+        "chunk_b4h16n2048nk16384d128_bf16_causal_bwd", B=4, H=16, N=2048, d=128,
+        dtype="bf16", causal=True, n_k=16384, backward=True, seed=1007),
+}
+
 
 @dataclasses.dataclass
 class Inputs:
@@ -102,9 +122,17 @@ def make_inputs(w: Workload, *, seed: Optional[int] = None) -> Inputs:
             x = x * std
         return x.to(dt)
 
+    kshape = (w.B, w.H, w.Nk, w.d)
+
+    def draw_k(std: float) -> torch.Tensor:
+        x = torch.randn(kshape, generator=g, dtype=torch.float32)
+        if std != 1.0:
+            x = x * std
+        return x.to(dt)
+
     q = draw(w.qk_std)
-    k = draw(w.qk_std)
-    v = draw(1.0)
+    k = draw_k(w.qk_std)
+    v = draw_k(1.0)
     do = draw(1.0) if w.backward else None
     kv_len = None
     if w.pad:

@@ -19,6 +19,10 @@ Prints ONE JSON line. Options:
   --no-per-config     skip the forward timings on each named workload (the
                       `forward_per_config` field: median and minimum per
                       launch, roofline fractions, one cold launch at N=4096)
+  --no-variants       skip the masked variants (the `variants` field: a
+                      sliding window of 4096 keys at N=16384, and a 2048-query
+                      chunk against 16384 keys, each forward and forward +
+                      backward, TFLOP/s over the visible query-key pairs)
   --unfused           also time standard attention as separate torch ops
                       (matmul, mask, softmax, dropout, matmul; the backward
                       by hand for the backward workload) against the fused
@@ -200,6 +204,84 @@ def per_config_forward(attn, W, dev, reuse=None, min_iters=50, min_ms=200.0) -> 
     return out
 
 
+def visible_pairs(w) -> float:
+    """Query-key pairs a masked variant computes per head: row i sees keys
+    [max(0, c - left), min(Nk - 1, c, c + right)] with c = i + Nk - N (causal
+    caps at c; -1 leaves a window side open)."""
+    import numpy as np
+    i = np.arange(w.N, dtype=np.int64)
+    c = i + (w.Nk - w.N)
+    lo = np.zeros_like(i)
+    hi = np.full_like(i, w.Nk - 1)
+    if w.causal:
+        hi = np.minimum(hi, c)
+    if w.window is not None:
+        if w.window[0] >= 0:
+            lo = np.maximum(lo, c - w.window[0])
+        if w.window[1] >= 0:
+            hi = np.minimum(hi, c + w.window[1])
+    return float(np.maximum(0, hi - lo + 1).sum())
+
+
+def variant_timings(attn, W, dev, reps: int = 30) -> dict:
+    """The masked variants (sliding window; non-square grid): forward alone and
+    forward + the three backward kernels, each launch bracketed by HIP events
+    on the launch stream after 5 warm-up passes; medians. FLOP count the pairs
+    actually visible: forward 4*d per pair, backward 2.5x that."""
+    import torch
+    out = {}
+    for name, w in W.VARIANTS.items():
+        inp = W.make_inputs(w)
+        q, k, v, do = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.do))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        kw = dict(causal=w.causal, window=w.window, scale=w.scale)
+        ws = torch.empty(attn.bwd_workspace_bytes(q, k=k, **kw), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            attn.fwd(q, k, v, out=o, lse=lse, **kw)
+
+        def bwd():
+            attn.bwd(q, k, v, o, lse, do, out=grads, workspace=ws, **kw)
+
+        for _ in range(5):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        tf, tb = [], []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            fwd()
+            e[1].record()
+            bwd()
+            e[2].record()
+            torch.cuda.synchronize()
+            tf.append(e[0].elapsed_time(e[1]))
+            tb.append(e[1].elapsed_time(e[2]))
+        tf.sort()
+        tb.sort()
+        fm, bm = tf[len(tf) // 2], tb[len(tb) // 2]
+        pairs = visible_pairs(w) * w.B * w.H
+        f_fwd = 4.0 * w.d * pairs
+        fwd_tf = f_fwd / (fm * 1e-3) / 1e12
+        step_tf = 3.5 * f_fwd / ((fm + bm) * 1e-3) / 1e12
+        out[name] = {
+            "B": w.B, "H": w.H, "N": w.N, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+            "window": list(w.window) if w.window else None,
+            "visible_pairs_per_head": int(pairs / (w.B * w.H)),
+            "fwd_ms": round(fm, 4), "bwd_ms": round(bm, 4),
+            "fwd_tflops": round(fwd_tf, 1),
+            "fwd_pct_of_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+            "fwd_bwd_tflops": round(step_tf, 1),
+            "fwd_bwd_pct_of_peak": round(100 * step_tf / PEAK_BF16_TFLOPS, 2),
+        }
+        del q, k, v, do, o, lse, grads, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) -> dict:
     """Standard attention as separate torch ops against the fused kernels, on
     every named workload: S = scale*Q K^T materialised in the input dtype,
@@ -345,6 +427,8 @@ def main() -> int:
                     help="add the unfused torch comparison on every workload")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip timing the forward on each named workload")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip timing the sliding-window and non-square variants")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only the forward headline workload (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -521,6 +605,8 @@ def main() -> int:
     if not args.no_per_config:
         out["forward_per_config"] = per_config_forward(
             attn, W, dev, reuse={WORKLOAD: (q, k, v, None)})
+    if not args.no_variants:
+        out["variants"] = variant_timings(attn, W, dev)
     if args.unfused:
         out["unfused_comparison"] = unfused_comparison(attn, W, dev)
     if not args.no_cpu_baseline:
