@@ -160,17 +160,32 @@ void attn_fwd_kernel(const FwdArgs a) {
 
   // Scores of one tile: S^T = K Q^T, 32 keys x 32 queries per block. The
   // NKB accumulator chains are interleaved step by step: a single chain of
-  // dependent MFMAs cannot issue at the full rate.
-  auto scores = [&](const char* kb, f32x16 (&s)[NKB], auto&& after_step) {
+  // dependent MFMAs cannot issue at the full rate. The K fragments of step
+  // kk + 1 are read from LDS before the MFMAs of step kk, in program order
+  // ahead of before_step (which may issue tile copies: the copies are inline
+  // assembly that no memory access moves across), so the MFMAs do not wait
+  // for their operands' LDS latency. after_step runs VALU work of the
+  // caller's between the steps' MFMAs.
+  auto scores = [&](const char* kb, f32x16 (&s)[NKB], auto&& before_step,
+                    auto&& after_step) {
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb2][r] = 0.f;
+    u32x4 kf[2][NKB];
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+      kf[0][kb2] = *(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[0]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2)
-        s[kb2] = E::mfma(*(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk]), qf[kk], s[kb2]);
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+          kf[(kk + 1) & 1][kb2] = *(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk + 1]);
+      }
+      before_step(kk);
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2) s[kb2] = E::mfma(kf[kk & 1][kb2], qf[kk], s[kb2]);
       after_step(kk);
     }
   };
@@ -227,7 +242,7 @@ void attn_fwd_kernel(const FwdArgs a) {
     __syncthreads();
     if (t0 + 1 < ntiles) loader.issue_one_untracked(K, (t0 + 1) * BC, kv_end, kb0 + TILE_BYTES);
     if (ntiles_w > t0) {
-      scores(kb0, ss[0], no_hook);
+      scores(kb0, ss[0], no_hook, no_hook);
       if (need_mask(t0 * BC)) mask(ss[0], t0 * BC);
       rescale(row_max(ss[0]));
     }
@@ -252,6 +267,33 @@ void attn_fwd_kernel(const FwdArgs a) {
     const int k0 = t * BC;
     const char* kbn = kb0 + (buf ^ 1) * TILE_BYTES;
     const char* vb = vb0 + buf * TILE_BYTES;
+    // Probabilities of tile t (log2 domain for v_exp_f32), PER of them after
+    // each k-step of S(t+1), in key order; each adjacent pair is rounded into
+    // the MFMA B operand of the PV product as soon as it exists. l sums the
+    // fp32 probabilities, lr the rounded ones.
+    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
+    float rs = 0.f;
+    float rr_sum = 0.f;
+    u32x4 pf[NC16];
+    constexpr int PER = NKB * 16 / KK;
+    auto exps = [&](int kk) {
+#pragma unroll
+      for (int u = 0; u < PER; u += 2) {
+        const int e = kk * PER + u;
+        const int kb2 = e >> 4;
+        const int r = e & 15;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb2][r], c2, -mb));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb2][r + 1], c2, -mb));
+        rs += p0;
+        rs += p1;
+        sc[kb2][r] = p0;
+        sc[kb2][r + 1] = p1;
+        const int c = kb2 * 2 + (r >> 3);
+        const int ee = (r & 7) >> 1;
+        pf[c][ee] = E::pack2(p0, p1);
+        rr_sum = E::add_pair(pf[c][ee], rr_sum);
+      }
+    };
     scores(kbn, sn, [&](int kk) {
       if constexpr (SPREAD) {
         constexpr int per = KK / (2 * SPW) > 0 ? KK / (2 * SPW) : 1;
@@ -263,32 +305,10 @@ void attn_fwd_kernel(const FwdArgs a) {
             loader.issue_slice_full(V, (t + 1) * BC, vb0 + (buf ^ 1) * TILE_BYTES, i - SPW);
         }
       }
-    });
-    // Probabilities of tile t (log2 domain for v_exp_f32).
-    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
-    float rs = 0.f;
+    }, no_hook);
 #pragma unroll
-    for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb2][r], c2, -mb));
-        rs += p;
-        sc[kb2][r] = p;
-      }
+    for (int kk = 0; kk < KK; ++kk) exps(kk);
     l += rs;
-    // P^T as MFMA B operands: 16 keys per step, 8 per lane.
-    u32x4 pf[NC16];
-    float rr_sum = 0.f;
-#pragma unroll
-    for (int c = 0; c < NC16; ++c) {
-      const int kb2 = c >> 1;
-      const int rr = (c & 1) * 8;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[c][e] = E::pack2(sc[kb2][rr + 2 * e], sc[kb2][rr + 2 * e + 1]);
-        rr_sum = E::add_pair(pf[c][e], rr_sum);
-      }
-    }
     lr += rr_sum;
     if (DROPOUT) {
 #pragma unroll
@@ -312,17 +332,21 @@ void attn_fwd_kernel(const FwdArgs a) {
       }
     }
     // O^T += V^T P^T. Lane (group g = lane/16, i = lane%16) addresses row
-    // 16c + 4hh + i/4 (+8) and columns 32db + 16(g&1) + 4(i&3) .. +4.
+    // 16c + 4hh + i/4 (+8) and columns 32db + 16(g&1) + 4(i&3) .. +4. The V
+    // fragment of the next MFMA is read before the current one is issued.
+    auto vfrag = [&](int i) {
+      const int c = i / NDB;
+      const int db = i % NDB;
+      const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[0][db]));
+      const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[1][db]));
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 vf[2];
+    vf[0] = vfrag(0);
 #pragma unroll
-    for (int c = 0; c < NC16; ++c) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2 lo = __builtin_bit_cast(
-            u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[0][db]));
-        const u32x2 hi = __builtin_bit_cast(
-            u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[1][db]));
-        acc[db] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[c], acc[db]);
-      }
+    for (int i = 0; i < NC16 * NDB; ++i) {
+      if (i + 1 < NC16 * NDB) vf[(i + 1) & 1] = vfrag(i + 1);
+      acc[i % NDB] = E::mfma(vf[i & 1], pf[i / NDB], acc[i % NDB]);
     }
     // Maximum of tile t+1 beside the PV MFMAs; a tile that needs a mask is
     // masked afterwards and its maximum taken again. After a wave's last tile
