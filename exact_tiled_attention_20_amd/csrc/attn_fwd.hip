@@ -267,10 +267,11 @@ void attn_fwd_kernel(const FwdArgs a) {
     const int k0 = t * BC;
     const char* kbn = kb0 + (buf ^ 1) * TILE_BYTES;
     const char* vb = vb0 + buf * TILE_BYTES;
-    // Probabilities of tile t (log2 domain for v_exp_f32), PER of them after
-    // each k-step of S(t+1), in key order; each adjacent pair is rounded into
-    // the MFMA B operand of the PV product as soon as it exists. l sums the
-    // fp32 probabilities, lr the rounded ones.
+    // Probabilities of tile t (log2 domain for v_exp_f32), in key order, PER
+    // per group; each adjacent pair is rounded into the MFMA B operand of the
+    // PV product as soon as it exists. l sums the fp32 probabilities, lr the
+    // rounded ones. (Placing the groups between the k-steps of S(t+1) was
+    // measured slower than running them after the S(t+1) MFMAs.)
     const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
     float rs = 0.f;
     float rr_sum = 0.f;
