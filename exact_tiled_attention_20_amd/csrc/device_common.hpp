@@ -155,18 +155,21 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
 // Rows at or past `valid` repeat row valid-1 (finite data the caller masks).
 // The same 16-byte copy written as inline assembly: base is wave-uniform,
 // voff is this lane's byte offset, lds_base the wave-uniform destination.
-// Writing M0 needs one wait state before the copy reads it. The copy counts
+// Writing M0 needs one wait state before the copy reads it. M0 is declared as
+// an output of the statement, so the compiler knows its value changed (M0 is
+// a reserved register and cannot appear in a clobber list). The copy counts
 // against vmcnt like any vector load.
 __device__ __forceinline__ void load_lds16_untracked(const void* base, uint32_t voff,
                                                      void* lds_base) {
   const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_t*)lds_base;
+  uint32_t m0_out;
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
+      "global_load_lds_dwordx4 %1, %2"
+      : "={m0}"(m0_out)
       : "v"(voff), "s"(base), "s"(m0v)
-      : "memory", "m0");
+      : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding
