@@ -85,11 +85,12 @@ WORKLOADS = {
 # Order matters: the first is the small case, the third is the headline forward.
 WORKLOAD_ORDER = list(WORKLOADS)
 
-# The masked variants the method's description names as needing tiling changes
-# (sliding-window attention, cross-attention on a non-square grid), at the
-# sizes of the 16K-context layer: a Mistral-style causal window of 4096 keys,
-# and a 2048-query chunk attending causally (bottom-right) to a 16384-key
-# context, as in chunked prefill against a key/value cache.
+# The variants the method's description names as needing tiling changes
+# (sliding-window attention, cross-attention on a non-square grid, head
+# dimension 256), at the sizes of the 16K-context layer: a Mistral-style causal
+# window of 4096 keys, a 2048-query chunk attending causally (bottom-right) to
+# a 16384-key context, as in chunked prefill against a key/value cache, and
+# d = 256.
 VARIANTS = {
     "swa4096_b1h32n16384d128_bf16_bwd": Workload(
         "swa4096_b1h32n16384d128_bf16_bwd", B=1, H=32, N=16384, d=128, dtype="bf16",
@@ -97,6 +98,11 @@ VARIANTS = {
     "chunk_b4h16n2048nk16384d128_bf16_causal_bwd": Workload(
         "chunk_b4h16n2048nk16384d128_bf16_causal_bwd", B=4, H=16, N=2048, d=128,
         dtype="bf16", causal=True, n_k=16384, backward=True, seed=1007),
+    # Head dimension 256 (forward only), the same token and FLOP budget per
+    # layer as the 16K-context layer with half the heads.
+    "d256_b1h16n16384_bf16_causal": Workload(
+        "d256_b1h16n16384_bf16_causal", B=1, H=16, N=16384, d=256, dtype="bf16",
+        causal=True, seed=1008),
 }
 
 

@@ -19,10 +19,11 @@ Prints ONE JSON line. Options:
   --no-per-config     skip the forward timings on each named workload (the
                       `forward_per_config` field: median and minimum per
                       launch, roofline fractions, one cold launch at N=4096)
-  --no-variants       skip the masked variants (the `variants` field: a
-                      sliding window of 4096 keys at N=16384, and a 2048-query
-                      chunk against 16384 keys, each forward and forward +
-                      backward, TFLOP/s over the visible query-key pairs)
+  --no-variants       skip the variants (the `variants` field: a sliding
+                      window of 4096 keys at N=16384 and a 2048-query chunk
+                      against 16384 keys, each forward and forward +
+                      backward, TFLOP/s over the visible query-key pairs; and
+                      the forward at head dimension 256)
   --unfused           also time standard attention as separate torch ops
                       (matmul, mask, softmax, dropout, matmul; the backward
                       by hand for the backward workload) against the fused
@@ -224,26 +225,32 @@ def visible_pairs(w) -> float:
 
 
 def variant_timings(attn, W, dev, reps: int = 30) -> dict:
-    """The masked variants (sliding window; non-square grid): forward alone and
-    forward + the three backward kernels, each launch bracketed by HIP events
-    on the launch stream after 5 warm-up passes; medians. FLOP count the pairs
-    actually visible: forward 4*d per pair, backward 2.5x that."""
+    """The variants (sliding window; non-square grid; d = 256): forward alone
+    and, where the workload has one, forward + the three backward kernels,
+    each bracketed by HIP events on the launch stream after 5 warm-up passes;
+    medians. FLOP count the pairs actually visible: forward 4*d per pair,
+    backward 2.5x that."""
     import torch
     out = {}
     for name, w in W.VARIANTS.items():
         inp = W.make_inputs(w)
-        q, k, v, do = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.do))
+        q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+        do = inp.do.to(dev) if w.backward else None
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         kw = dict(causal=w.causal, window=w.window, scale=w.scale)
-        ws = torch.empty(attn.bwd_workspace_bytes(q, k=k, **kw), dtype=torch.uint8, device=dev)
+        grads = ws = None
+        if w.backward:
+            grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+            ws = torch.empty(attn.bwd_workspace_bytes(q, k=k, **kw), dtype=torch.uint8,
+                             device=dev)
 
         def fwd():
             attn.fwd(q, k, v, out=o, lse=lse, **kw)
 
         def bwd():
-            attn.bwd(q, k, v, o, lse, do, out=grads, workspace=ws, **kw)
+            if w.backward:
+                attn.bwd(q, k, v, o, lse, do, out=grads, workspace=ws, **kw)
 
         for _ in range(5):
             fwd()
@@ -266,17 +273,19 @@ def variant_timings(attn, W, dev, reps: int = 30) -> dict:
         pairs = visible_pairs(w) * w.B * w.H
         f_fwd = 4.0 * w.d * pairs
         fwd_tf = f_fwd / (fm * 1e-3) / 1e12
-        step_tf = 3.5 * f_fwd / ((fm + bm) * 1e-3) / 1e12
+        step_tf = 3.5 * f_fwd / ((fm + bm) * 1e-3) / 1e12 if w.backward else None
         out[name] = {
             "B": w.B, "H": w.H, "N": w.N, "Nk": w.Nk, "d": w.d, "causal": w.causal,
             "window": list(w.window) if w.window else None,
             "visible_pairs_per_head": int(pairs / (w.B * w.H)),
-            "fwd_ms": round(fm, 4), "bwd_ms": round(bm, 4),
+            "fwd_ms": round(fm, 4),
             "fwd_tflops": round(fwd_tf, 1),
             "fwd_pct_of_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
-            "fwd_bwd_tflops": round(step_tf, 1),
-            "fwd_bwd_pct_of_peak": round(100 * step_tf / PEAK_BF16_TFLOPS, 2),
         }
+        if w.backward:
+            out[name].update({
+                "bwd_ms": round(bm, 4), "fwd_bwd_tflops": round(step_tf, 1),
+                "fwd_bwd_pct_of_peak": round(100 * step_tf / PEAK_BF16_TFLOPS, 2)})
         del q, k, v, do, o, lse, grads, ws
         torch.cuda.empty_cache()
     return out

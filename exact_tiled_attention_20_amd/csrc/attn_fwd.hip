@@ -42,7 +42,8 @@
 namespace attn {
 
 template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
-__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kFwdThreads)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void attn_fwd_kernel(const FwdArgs a) {
   constexpr int BR = kFwdBlockQ;
   constexpr int BC = kFwdBlockK;
@@ -457,9 +458,11 @@ static hipError_t launch_d(int mask, bool dropout, bool out_f32, const FwdArgs& 
 hipError_t launch_fwd(int dtype, int d, int mask, bool dropout, bool out_f32,
                       const FwdArgs& a, hipStream_t stream) {
   if (dtype == 1) {
+    if (d == 256) return launch_d<Elem<bf16_t>, 256>(mask, dropout, out_f32, a, stream);
     if (d == 128) return launch_d<Elem<bf16_t>, 128>(mask, dropout, out_f32, a, stream);
     return launch_d<Elem<bf16_t>, 64>(mask, dropout, out_f32, a, stream);
   }
+  if (d == 256) return launch_d<Elem<f16_t>, 256>(mask, dropout, out_f32, a, stream);
   if (d == 128) return launch_d<Elem<f16_t>, 128>(mask, dropout, out_f32, a, stream);
   return launch_d<Elem<f16_t>, 64>(mask, dropout, out_f32, a, stream);
 }

@@ -129,7 +129,9 @@ __device__ __forceinline__ u32x4 dropout_draws(uint32_t t, uint32_t i, uint32_t 
 // next row bits, so both patterns touch every bank once per 256 bytes.
 template <int D>
 __device__ __forceinline__ int lds_swz(int row) {
-  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  // d = 256 rows span two 256-byte bank rounds; the bank group of a chunk is
+  // its index mod 16, so the d = 128 mask (4 bits) serves both.
+  if (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 

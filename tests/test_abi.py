@@ -85,7 +85,7 @@ INVALID = [
     dict(n_k=-1), dict(window=(-2, 0)), dict(window=(0, -7)),
 ]
 UNSUPPORTED = [
-    dict(d=96), dict(d=256), dict(d=32),
+    dict(d=96), dict(d=512), dict(d=32),
     dict(dtype=attn.ATTN_F32, out_dtype=attn.ATTN_F32),
     dict(dtype=attn.ATTN_F16, out_dtype=attn.ATTN_BF16),
 ]
@@ -200,3 +200,16 @@ def test_aliasing_checks_cover_the_key_rows(lib):
     ptrs = _ptrs(10)
     ptrs[7] = ptrs[1] + 2 * 3 * 500 * 64 * 2          # dk inside k's key rows
     assert _bwd(lib, p, ptrs) == 1
+
+
+def test_head_dim_256_is_forward_only(lib):
+    """d = 256 has a forward kernel; the backward reports it unsupported
+    (never a fallback), and so does its workspace query (0 bytes)."""
+    p = _params(d=256)
+    assert _bwd(lib, p) == 2
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p)) == 0
+    q, k, v, o, lse, do, dq, dk, dv, ws = _ptrs(10)
+    assert lib.attn_bwd_stage(ctypes.byref(p), 1, q, k, v, o, lse, do, dq, dk, dv,
+                              ws, 1 << 30, None) == 2
+    bad = _params(d=256, scale=0.0)       # argument errors still come first
+    assert _fwd(lib, bad) == 1 and _bwd(lib, bad) == 1
