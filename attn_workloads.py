@@ -98,11 +98,11 @@ VARIANTS = {
     "chunk_b4h16n2048nk16384d128_bf16_causal_bwd": Workload(
         "chunk_b4h16n2048nk16384d128_bf16_causal_bwd", B=4, H=16, N=2048, d=128,
         dtype="bf16", causal=True, n_k=16384, backward=True, seed=1007),
-    # Head dimension 256 (forward only), the same token and FLOP budget per
-    # layer as the 16K-context layer with half the heads.
-    "d256_b1h16n16384_bf16_causal": Workload(
-        "d256_b1h16n16384_bf16_causal", B=1, H=16, N=16384, d=256, dtype="bf16",
-        causal=True, seed=1008),
+    # Head dimension 256: the same tokens and FLOP per layer as the 16K-context
+    # layer with half the heads.
+    "d256_b1h16n16384_bf16_causal_bwd": Workload(
+        "d256_b1h16n16384_bf16_causal_bwd", B=1, H=16, N=16384, d=256, dtype="bf16",
+        causal=True, backward=True, seed=1008),
 }
 
 

@@ -13,8 +13,8 @@ the module raises if the library is missing or a call fails.
     keep = dropout_mask(B, H, N, dropout_p, seed, device, n_k=None)
 
 q and dO are (B, H, N, d); k and v are (B, H, Nk, d) (Nk = N for
-self-attention), contiguous, float16 or bfloat16, d in {64, 128, 256}
-(256: forward only). Query i lines up with key i + Nk - N. window =
+self-attention), contiguous, float16 or bfloat16, d in {64, 128, 256}.
+Query i lines up with key i + Nk - N. window =
 (left, right) keeps keys at most `left` before and `right` after that key
 (-1: unbounded side).
 """

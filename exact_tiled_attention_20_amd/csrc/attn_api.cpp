@@ -68,11 +68,11 @@ attn_status check_params(const attn_params* p) {
   return ATTN_OK;
 }
 
-// The backward kernels exist for d = 64 and 128 (d = 256 is forward only).
+// The backward has every combination above except d = 256 with dropout.
 attn_status check_bwd_params(const attn_params* p) {
   const attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
-  if (p->d == 256) return ATTN_ERR_UNSUPPORTED;
+  if (p->d == 256 && p->dropout_p > 0.0f) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 

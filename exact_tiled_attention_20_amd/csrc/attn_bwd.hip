@@ -80,12 +80,17 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs 
 // d = 128 that fills the 160 KiB of LDS exactly); lse and D of the tile's rows
 // are read from L2 into registers.
 constexpr int kDkdvWaves = 8;
-constexpr int kDkdvThreads = 64 * kDkdvWaves;
+// d = 256: 4 waves (128 keys, 128 KiB of K/V rows) at one wave per SIMD, and a
+// single Q tile and dO tile of 16 KiB each: 160 KiB of LDS in all.
+template <int D>
+constexpr int dkdv_waves() { return D > 128 ? 4 : kDkdvWaves; }
 
 template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
-__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * dkdv_waves<D>())
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void attn_bwd_dkdv_kernel(const BwdArgs a) {
-  constexpr int NW = kDkdvWaves;
+  constexpr int NW = dkdv_waves<D>();
+  constexpr bool DBUF = D <= 128;      // double-buffered Q / dO tiles
   constexpr int BKW = 32 * NW;         // keys per workgroup
   constexpr int BQ = 32;               // query rows per tile
   constexpr int KK = D / 16;
@@ -101,10 +106,11 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   // rows followed by its 32 V rows, so both are addressed from one per-lane
   // base.
   constexpr int KV_WAVE = 32 * D * 2;            // K (or V) rows of one wave
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES + 2 * KV_BYTES];
-  char* const qb0 = smem;                        // [2] Q tiles
-  char* const ob0 = smem + 2 * TILE_BYTES;       // [2] dO tiles
-  constexpr int KVB = 4 * TILE_BYTES;            // byte offset of the per-wave K/V blocks
+  constexpr int NBUF = DBUF ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * TILE_BYTES + 2 * KV_BYTES];
+  char* const qb0 = smem;                        // [NBUF] Q tiles
+  char* const ob0 = smem + NBUF * TILE_BYTES;    // [NBUF] dO tiles
+  constexpr int KVB = 2 * NBUF * TILE_BYTES;     // byte offset of the per-wave K/V blocks
 
   const int nkb = (a.Nk + BKW - 1) / BKW;
   const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, nkb);
@@ -197,11 +203,8 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     if (qt0 < nqt) issue_tile(qt0, 0);
     // Unrolled by two (one instantiation per buffer), so LDS addresses carry
     // the buffer offset as an immediate.
-    auto tile_step = [&](int t, auto buf_c) {
-      constexpr int buf = decltype(buf_c)::value;
-      wait_all_memory();
-      __syncthreads();
-      if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
+    auto tile_compute = [&](int t, auto buf_c) {
+      constexpr int buf = DBUF ? decltype(buf_c)::value : 0;
       const int qbase = t * BQ;
       const bool active = wave_has_keys &&
                           (!BAND || (qbase + 31 >= kw - band_hi &&
@@ -302,6 +305,20 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
         }
       }
     };
+    auto tile_step = [&](int t, auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;
+      wait_all_memory();
+      __syncthreads();
+      if constexpr (DBUF) {
+        if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
+      }
+      tile_compute(t, buf_c);
+      if constexpr (!DBUF) {
+        // One buffer: the next tile is copied once every wave has read this one.
+        __syncthreads();
+        if (t + 1 < nqt) issue_tile(t + 1, 0);
+      }
+    };
     for (int t = qt0; t < nqt; t += 2) {
       tile_step(t, std::integral_constant<int, 0>());
       if (t + 1 < nqt) tile_step(t + 1, std::integral_constant<int, 1>());
@@ -338,7 +355,8 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
 // keys are copied HBM -> LDS directly; each tile is processed as two 32-key
 // halves to keep two waves per SIMD.
 template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kBwdThreads)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void attn_bwd_dq_kernel(const BwdArgs a) {
   constexpr int BR = 128;
   constexpr int BC = 64;
@@ -557,10 +575,11 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 1) {
-    const int nkb = (a.Nk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
+    constexpr int NW = dkdv_waves<D>();
+    const int nkb = (a.Nk + 32 * NW - 1) / (32 * NW);
     const int tk = a.B * a.H * nkb;
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<E, D, MASK, DROPOUT, OUT_F32>),
-                       dim3(((tk + 7) / 8) * 8), dim3(kDkdvThreads), 0, stream, a);
+                       dim3(((tk + 7) / 8) * 8), dim3(64 * NW), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -576,8 +595,15 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
 
 template <typename E, int D, int MASK>
 static hipError_t launch_m(bool dropout, bool out_f32, int st, const BwdArgs& a, hipStream_t s) {
-  if (dropout) return out_f32 ? launch_all<E, D, MASK, true, true>(st, a, s)
-                              : launch_all<E, D, MASK, true, false>(st, a, s);
+  // No d = 256 backward with dropout: hipcc 7.2 (clang 22) crashes in its
+  // AGPR-copy rewrite pass on that dK/dV instantiation. The host API rejects
+  // the combination before anything is launched.
+  if constexpr (D > 128) {
+    if (dropout) return hipErrorNotSupported;
+  } else if (dropout) {
+    return out_f32 ? launch_all<E, D, MASK, true, true>(st, a, s)
+                   : launch_all<E, D, MASK, true, false>(st, a, s);
+  }
   return out_f32 ? launch_all<E, D, MASK, false, true>(st, a, s)
                  : launch_all<E, D, MASK, false, false>(st, a, s);
 }
@@ -593,9 +619,11 @@ static hipError_t launch_d(int mask, bool dropout, bool out_f32, int st, const B
 hipError_t launch_bwd(int dtype, int d, int mask, bool dropout, bool out_f32, int stage,
                       const BwdArgs& a, hipStream_t stream) {
   if (dtype == 1) {
+    if (d == 256) return launch_d<Elem<bf16_t>, 256>(mask, dropout, out_f32, stage, a, stream);
     if (d == 128) return launch_d<Elem<bf16_t>, 128>(mask, dropout, out_f32, stage, a, stream);
     return launch_d<Elem<bf16_t>, 64>(mask, dropout, out_f32, stage, a, stream);
   }
+  if (d == 256) return launch_d<Elem<f16_t>, 256>(mask, dropout, out_f32, stage, a, stream);
   if (d == 128) return launch_d<Elem<f16_t>, 128>(mask, dropout, out_f32, stage, a, stream);
   return launch_d<Elem<f16_t>, 64>(mask, dropout, out_f32, stage, a, stream);
 }

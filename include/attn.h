@@ -92,8 +92,8 @@ typedef enum {
 typedef struct {
   int32_t B, H, N, d;      /* batch, heads, sequence length, head dim.
                               B, H, N >= 1; d in {64, 128, 256}
-                              (d = 256: forward only; the backward
-                              returns ATTN_ERR_UNSUPPORTED);
+                              (the backward has no d = 256 kernel with
+                              dropout: ATTN_ERR_UNSUPPORTED);
                               N*d and Nk*d must be below 2^31 (per-head
                               index math) and the element counts of every
                               tensor below about 2^62.                     */

@@ -202,14 +202,15 @@ def test_aliasing_checks_cover_the_key_rows(lib):
     assert _bwd(lib, p, ptrs) == 1
 
 
-def test_head_dim_256_is_forward_only(lib):
-    """d = 256 has a forward kernel; the backward reports it unsupported
-    (never a fallback), and so does its workspace query (0 bytes)."""
+def test_head_dim_256_is_supported(lib):
+    """d = 256 passes validation for forward and backward: with the fake
+    pointers every check passes up to aliasing, which is then reported."""
     p = _params(d=256)
-    assert _bwd(lib, p) == 2
-    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p)) == 0
-    q, k, v, o, lse, do, dq, dk, dv, ws = _ptrs(10)
-    assert lib.attn_bwd_stage(ctypes.byref(p), 1, q, k, v, o, lse, do, dq, dk, dv,
-                              ws, 1 << 30, None) == 2
-    bad = _params(d=256, scale=0.0)       # argument errors still come first
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p)) == 2 * (((2 * 3 * 100 * 4 + 255) // 256) * 256)
+    q, k, v, o, lse = _ptrs(5)
+    assert _fwd(lib, p, [q, k, v, q, lse]) == 1      # o aliases q: rejected, not unsupported
+    bad = _params(d=256, scale=0.0)
     assert _fwd(lib, bad) == 1 and _bwd(lib, bad) == 1
+    drop = _params(d=256, dropout_p=0.1)           # no d = 256 backward with dropout
+    assert _bwd(lib, drop) == 2
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(drop)) == 0

@@ -1,9 +1,10 @@
-"""GPU parity at the full sizes of the two masked variants the benchmark
-times: a Mistral-style sliding window of 4096 keys over a 16K-token causal
-layer (B=1, H=32, N=16384, d=128, bf16), and a 2048-query chunk attending
-causally, bottom-right aligned, to a 16384-key context (B=4, H=16, d=128,
-bf16), each forward + backward in the launch configuration the benchmark uses
-(outputs in the input dtype) and in the float32-output mode.
+"""GPU parity at the full sizes of the variants the benchmark times: a
+Mistral-style sliding window of 4096 keys over a 16K-token causal layer (B=1,
+H=32, N=16384, d=128, bf16), a 2048-query chunk attending causally,
+bottom-right aligned, to a 16384-key context (B=4, H=16, d=128, bf16), and
+head dimension 256 (B=1, H=16, N=16384, causal, bf16), each forward +
+backward in the launch configuration the benchmark uses (outputs in the input
+dtype) and in the float32-output mode.
 
 The oracle checks sampled heads: on sampled query rows (O, lse, dQ) and key
 columns (dK, dV), each evaluated from the definition ("Why FlashAttention Is
@@ -28,7 +29,7 @@ def _say(msg):
     sys.stdout.flush()
 
 
-@pytest.fixture(scope="module", params=[n for n, w in W.VARIANTS.items() if w.backward])
+@pytest.fixture(scope="module", params=list(W.VARIANTS))
 def variant_gpu(request):
     w = W.VARIANTS[request.param]
     inp = W.make_inputs(w)
@@ -84,22 +85,3 @@ def test_variant_gradient_invariants(variant_gpu):
     _say(f"[{w.name}] max|sum_j dK_j| {sk:.3e}, max|sum_j dV_j - sum_i dO_i| {dsv:.3e}")
     assert sk < 1.0 and dsv < 1.0
 
-
-def test_d256_forward_sampled():
-    """Head dimension 256, B=1 H=16 N=16384 causal bf16, forward in both
-    output modes: three heads on sampled rows."""
-    w = W.VARIANTS["d256_b1h16n16384_bf16_causal"]
-    inp = W.make_inputs(w)
-    q, k, v = (t.to(DEV) for t in (inp.q, inp.k, inp.v))
-    rng = np.random.default_rng(w.seed)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 8191, w.N - 1], rng.integers(0, w.N, 90)]))
-    heads = [(0, 0), (0, w.H - 1), (0, int(rng.integers(w.H)))]
-    O_r, l_r = A.forward(inp.q, inp.k, inp.v, rows=rows, heads=heads, scale=w.scale, causal=True)
-    for odt in (inp.q.dtype, torch.float32):
-        o, lse = attn.fwd(q, k, v, causal=True, scale=w.scale, out_dtype=odt)
-        torch.cuda.synchronize()
-        o, lse = o.cpu(), lse.cpu()
-        for (b, h) in heads:
-            e, _ = check_close("O", o[b, h, rows], O_r[b, h], O_ATOL, odt)
-            check_lse(lse[b, h, rows], l_r[b, h])
-            _say(f"[{w.name}] head {(b, h)} out={odt}: max|err| O {e:.2e}")
