@@ -150,3 +150,24 @@ def test_band_fwd_bitwise_deterministic():
     b = attn.fwd(q, k, v, causal=True, window=(333, -1), scale=0.09)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_window_wider_than_int_range_equals_no_window():
+    """Window sides up to 2^31 - 1 are legal; the host clamps the band edges
+    to +-2^30 (beyond every index of a valid shape), so the result equals the
+    unmasked / causal one."""
+    big = 2**31 - 1
+    inp = W.random_case(1, 2, 333, 128, "bf16", seed=21, with_do=True, n_k=401)
+    q, k, v, do = (t.to(DEV) for t in (inp.q, inp.k, inp.v, inp.do))
+    for causal in (False, True):
+        O_ref, lse_ref = A.forward(inp.q, inp.k, inp.v, scale=0.09, causal=causal)
+        o, lse = attn.fwd(q, k, v, causal=causal, scale=0.09, window=(big, big),
+                          out_dtype=torch.float32)
+        g = attn.bwd(q, k, v, o, lse, do, causal=causal, scale=0.09, window=(big, big),
+                     out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        check_close("O", o, O_ref, O_ATOL, torch.float32)
+        check_lse(lse, lse_ref)
+        g_ref = A.backward(inp.q, inp.k, inp.v, inp.do, scale=0.09, causal=causal)
+        for name, got, ref in zip(("dQ", "dK", "dV"), g, g_ref):
+            check_close(name, got, ref, GRAD_ATOL, torch.float32)
