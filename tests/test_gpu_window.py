@@ -171,3 +171,18 @@ def test_window_wider_than_int_range_equals_no_window():
         g_ref = A.backward(inp.q, inp.k, inp.v, inp.do, scale=0.09, causal=causal)
         for name, got, ref in zip(("dQ", "dK", "dV"), g, g_ref):
             check_close(name, got, ref, GRAD_ATOL, torch.float32)
+
+
+@pytest.mark.parametrize("causal,window,p", [(True, None, 0.0), (False, (300, 40), 0.1)])
+def test_bwd_bitwise_deterministic(causal, window, p):
+    """dQ has its own kernel (no atomics): two backward passes on the same
+    inputs give identical bits."""
+    inp = W.random_case(2, 3, 900, 128, "bf16", seed=33, with_do=True, n_k=1100)
+    q, k, v, do = (t.to(DEV) for t in (inp.q, inp.k, inp.v, inp.do))
+    kw = dict(causal=causal, window=window, dropout_p=p, seed=inp.seed, scale=0.09)
+    o, lse = attn.fwd(q, k, v, **kw)
+    g1 = attn.bwd(q, k, v, o, lse, do, **kw)
+    g2 = attn.bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
