@@ -203,8 +203,13 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     if (qt0 < nqt) issue_tile(qt0, 0);
     // Unrolled by two (one instantiation per buffer), so LDS addresses carry
     // the buffer offset as an immediate.
-    auto tile_compute = [&](int t, auto buf_c) {
+    auto tile_step = [&](int t, auto buf_c) {
       constexpr int buf = DBUF ? decltype(buf_c)::value : 0;
+      wait_all_memory();
+      __syncthreads();
+      if constexpr (DBUF) {
+        if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
+      }
       const int qbase = t * BQ;
       const bool active = wave_has_keys &&
                           (!BAND || (qbase + 31 >= kw - band_hi &&
@@ -305,23 +310,19 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
         }
       }
     };
-    auto tile_step = [&](int t, auto buf_c) {
-      constexpr int buf = decltype(buf_c)::value;
-      wait_all_memory();
-      __syncthreads();
-      if constexpr (DBUF) {
-        if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
+    if constexpr (DBUF) {
+      for (int t = qt0; t < nqt; t += 2) {
+        tile_step(t, std::integral_constant<int, 0>());
+        if (t + 1 < nqt) tile_step(t + 1, std::integral_constant<int, 1>());
       }
-      tile_compute(t, buf_c);
-      if constexpr (!DBUF) {
-        // One buffer: the next tile is copied once every wave has read this one.
+    } else {
+      // One buffer: the next tile is copied once every wave has read this
+      // one (waves that skip a tile still meet both barriers).
+      for (int t = qt0; t < nqt; ++t) {
+        tile_step(t, std::integral_constant<int, 0>());
         __syncthreads();
         if (t + 1 < nqt) issue_tile(t + 1, 0);
       }
-    };
-    for (int t = qt0; t < nqt; t += 2) {
-      tile_step(t, std::integral_constant<int, 0>());
-      if (t + 1 < nqt) tile_step(t + 1, std::integral_constant<int, 1>());
     }
   }
 

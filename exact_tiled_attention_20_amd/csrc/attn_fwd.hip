@@ -173,21 +173,34 @@ void attn_fwd_kernel(const FwdArgs a) {
     for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb2][r] = 0.f;
-    u32x4 kf[2][NKB];
+    if constexpr (DROPOUT) {
+      // The dropout instances keep the operand reads beside their MFMAs:
+      // the Philox state leaves no registers for a second fragment set.
 #pragma unroll
-    for (int kb2 = 0; kb2 < NKB; ++kb2)
-      kf[0][kb2] = *(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[0]);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) {
+      for (int kk = 0; kk < KK; ++kk) {
+        before_step(kk);
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2)
-          kf[(kk + 1) & 1][kb2] = *(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk + 1]);
+          s[kb2] = E::mfma(*(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk]), qf[kk], s[kb2]);
+        after_step(kk);
       }
-      before_step(kk);
+    } else {
+      u32x4 kf[2][NKB];
 #pragma unroll
-      for (int kb2 = 0; kb2 < NKB; ++kb2) s[kb2] = E::mfma(kf[kk & 1][kb2], qf[kk], s[kb2]);
-      after_step(kk);
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
+        kf[0][kb2] = *(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[0]);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) {
+#pragma unroll
+          for (int kb2 = 0; kb2 < NKB; ++kb2)
+            kf[(kk + 1) & 1][kb2] = *(const u32x4*)(kb + kb2 * 32 * D * 2 + koff[kk + 1]);
+        }
+        before_step(kk);
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2) s[kb2] = E::mfma(kf[kk & 1][kb2], qf[kk], s[kb2]);
+        after_step(kk);
+      }
     }
   };
   auto no_hook = [](int) {};
@@ -308,8 +321,31 @@ void attn_fwd_kernel(const FwdArgs a) {
         }
       }
     }, no_hook);
+    if constexpr (DROPOUT) {
+      // One pass of exponentials, then one of packing: the order that keeps
+      // the dropout instances' registers lowest.
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) exps(kk);
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb2][r], c2, -mb));
+          rs += p;
+          sc[kb2][r] = p;
+        }
+#pragma unroll
+      for (int c = 0; c < NC16; ++c) {
+        const int kb2 = c >> 1;
+        const int rr = (c & 1) * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pf[c][e] = E::pack2(sc[kb2][rr + 2 * e], sc[kb2][rr + 2 * e + 1]);
+          rr_sum = E::add_pair(pf[c][e], rr_sum);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) exps(kk);
+    }
     l += rs;
     lr += rr_sum;
     if (DROPOUT) {
@@ -343,12 +379,17 @@ void attn_fwd_kernel(const FwdArgs a) {
       const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vb, c * 16 * D * 2 + voff[1][db]));
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
-    u32x4 vf[2];
-    vf[0] = vfrag(0);
+    if constexpr (DROPOUT) {
 #pragma unroll
-    for (int i = 0; i < NC16 * NDB; ++i) {
-      if (i + 1 < NC16 * NDB) vf[(i + 1) & 1] = vfrag(i + 1);
-      acc[i % NDB] = E::mfma(vf[i & 1], pf[i / NDB], acc[i % NDB]);
+      for (int i = 0; i < NC16 * NDB; ++i) acc[i % NDB] = E::mfma(vfrag(i), pf[i / NDB], acc[i % NDB]);
+    } else {
+      u32x4 vf[2];
+      vf[0] = vfrag(0);
+#pragma unroll
+      for (int i = 0; i < NC16 * NDB; ++i) {
+        if (i + 1 < NC16 * NDB) vf[(i + 1) & 1] = vfrag(i + 1);
+        acc[i % NDB] = E::mfma(vf[i & 1], pf[i / NDB], acc[i % NDB]);
+      }
     }
     // Maximum of tile t+1 beside the PV MFMAs; a tile that needs a mask is
     // masked afterwards and its maximum taken again. After a wave's last tile
