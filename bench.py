@@ -293,7 +293,7 @@ def variant_timings(attn, W, dev, reps: int = 30) -> dict:
 
 def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) -> dict:
     """Standard attention as separate torch ops against the fused kernels, on
-    every named workload: S = scale*Q K^T materialised in the input dtype,
+    every named workload and variant: S = scale*Q K^T materialised in the input dtype,
     mask by -inf, softmax, dropout (torch's own RNG: same work, different
     mask), O = P V; for the backward workload also dV = P^T dO,
     dP = dO V^T, D = rowsum(dO*O), dS = P*(dP - D), dQ = scale*dS K,
@@ -327,36 +327,49 @@ def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) 
         return torch.cuda.max_memory_allocated() - base
 
     out = {}
-    for name, w in W.WORKLOADS.items():
+    for name, w in dict(W.WORKLOADS, **W.VARIANTS).items():
         inp = W.make_inputs(w)
         q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
         kv = None if inp.kv_len is None else inp.kv_len.to(dev)
         do = None if inp.do is None else inp.do.to(dev)
         seed = W.DROPOUT_SEED if w.dropout_p > 0 else 0
-        reps = reps_large if w.N >= 4096 else reps_small
-        idx = torch.arange(w.N, device=dev)
+        reps = reps_large if w.N >= 4096 or w.Nk >= 4096 else reps_small
+        # Keys each query row may not see: past its causal or window bound
+        # (query i lines up with key i + Nk - N), or past the padding length.
+        i_idx = torch.arange(w.N, device=dev)[:, None] + (w.Nk - w.N)
+        j_idx = torch.arange(w.Nk, device=dev)[None, :]
         dead = None
         if w.causal:
-            dead = (idx[None, :] > idx[:, None])[None, None]
+            dead = (j_idx > i_idx)[None, None]
+        if w.window is not None:
+            if w.window[0] >= 0:
+                lo = (j_idx < i_idx - w.window[0])[None, None]
+                dead = lo if dead is None else (dead | lo)
+            if w.window[1] >= 0:
+                hi = (j_idx > i_idx + w.window[1])[None, None]
+                dead = hi if dead is None else (dead | hi)
         if kv is not None:
-            pad = (idx[None, :] >= kv[:, None].long())[:, None, None, :]
+            pad = (j_idx >= kv[:, None].long())[:, None, None, :]
             dead = pad if dead is None else (dead | pad)
         o_f = torch.empty_like(q)
         lse_f = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-        grads_f = tuple(torch.empty_like(q) for _ in range(3)) if do is not None else None
+        grads_f = None
+        if do is not None:
+            grads_f = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         ws = None
         if do is not None:
-            ws = torch.empty(attn.bwd_workspace_bytes(q, causal=w.causal, scale=w.scale),
+            ws = torch.empty(attn.bwd_workspace_bytes(q, k=k, causal=w.causal, scale=w.scale,
+                                                      window=w.window),
                              dtype=torch.uint8, device=dev)
         state = {}
 
         def fused():
             attn.fwd(q, k, v, causal=w.causal, kv_len=kv, dropout_p=w.dropout_p, seed=seed,
-                     scale=w.scale, out=o_f, lse=lse_f)
+                     scale=w.scale, out=o_f, lse=lse_f, window=w.window)
             if do is not None:
                 attn.bwd(q, k, v, o_f, lse_f, do, causal=w.causal, kv_len=kv,
                          dropout_p=w.dropout_p, seed=seed, scale=w.scale, out=grads_f,
-                         workspace=ws)
+                         workspace=ws, window=w.window)
 
         def transposes():
             kt = k.transpose(-1, -2).contiguous()
@@ -386,9 +399,9 @@ def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) 
                 state["g"] = (dq, dk, dv)
 
         def transposes_bwd():
-            # The two N x N transposed copies of the backward, on tensors of
+            # The two N x Nk transposed copies of the backward, on tensors of
             # the same shape and dtype as P and dS.
-            t = torch.empty(w.B, w.H, w.N, w.N, dtype=q.dtype, device=dev)
+            t = torch.empty(w.B, w.H, w.N, w.Nk, dtype=q.dtype, device=dev)
             t.transpose(-1, -2).contiguous()
             t.transpose(-1, -2).contiguous()
 
@@ -409,7 +422,11 @@ def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) 
         t_copy = timed(transposes, reps)
         if do is not None:
             t_copy += timed(transposes_bwd, reps)
-        flops = w.flops_fwd() + (w.flops_bwd() if do is not None else 0.0)
+        if name in W.VARIANTS:
+            f_fwd = 4.0 * w.d * visible_pairs(w) * w.B * w.H
+            flops = f_fwd * (3.5 if do is not None else 1.0)
+        else:
+            flops = w.flops_fwd() + (w.flops_bwd() if do is not None else 0.0)
         out[name] = {
             "pass": "fwd+bwd" if do is not None else "fwd",
             "fused_ms": round(t_fused, 4), "unfused_ms": round(t_unf, 4),
