@@ -186,3 +186,22 @@ def test_bwd_bitwise_deterministic(causal, window, p):
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("causal,window,nk", [(True, None, None), (True, (200, -1), 700),
+                                              (False, (40, 60), 450)])
+def test_bwd_stages_equal_bwd(causal, window, nk):
+    """attn_bwd_stage called for preprocess, dK/dV and dQ in that order on one
+    stream runs the same kernels as attn_bwd: identical bits."""
+    inp = W.random_case(2, 2, 500, 128, "bf16", seed=44, with_do=True, n_k=nk)
+    q, k, v, do = (t.to(DEV) for t in (inp.q, inp.k, inp.v, inp.do))
+    kw = dict(causal=causal, window=window, scale=0.09)
+    o, lse = attn.fwd(q, k, v, **kw)
+    g_all = attn.bwd(q, k, v, o, lse, do, **kw)
+    ws = torch.empty(attn.bwd_workspace_bytes(q, k=k, **kw), dtype=torch.uint8, device=DEV)
+    out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    for st in (attn.BWD_STAGE_PREPROCESS, attn.BWD_STAGE_DKDV, attn.BWD_STAGE_DQ):
+        attn.bwd(q, k, v, o, lse, do, out=out, workspace=ws, stage=st, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(g_all, out):
+        assert torch.equal(a, b)
