@@ -68,14 +68,6 @@ attn_status check_params(const attn_params* p) {
   return ATTN_OK;
 }
 
-// The backward has every combination above except d = 256 with dropout.
-attn_status check_bwd_params(const attn_params* p) {
-  const attn_status st = check_params(p);
-  if (st != ATTN_OK) return st;
-  if (p->d == 256 && p->dropout_p > 0.0f) return ATTN_ERR_UNSUPPORTED;
-  return ATTN_OK;
-}
-
 uint32_t drop_threshold(float p) {
   // floor(p * 2^32) is exact in double for a float p in [0, 1).
   return (uint32_t)std::floor((double)p * 4294967296.0);
@@ -181,7 +173,7 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
 }
 
 size_t attn_bwd_workspace_bytes(const attn_params* p) {
-  if (check_bwd_params(p) != ATTN_OK) return 0;
+  if (check_params(p) != ATTN_OK) return 0;
   // Two fp32 (B, H, N) arrays, each rounded up to 256 bytes: D_i = dO_i . O_i
   // and lse_i * log2(e).
   return 2 * ((stat_bytes(p) + 255) & ~size_t(255));
@@ -192,7 +184,7 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
                             void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, void* stream) {
   if (stage < -1 || stage > 2) return ATTN_ERR_INVALID_ARG;
-  attn_status st = check_bwd_params(p);
+  attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
   const void* ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
   for (const void* x : ptrs)

@@ -596,15 +596,8 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
 
 template <typename E, int D, int MASK>
 static hipError_t launch_m(bool dropout, bool out_f32, int st, const BwdArgs& a, hipStream_t s) {
-  // No d = 256 backward with dropout: hipcc 7.2 (clang 22) crashes in its
-  // AGPR-copy rewrite pass on that dK/dV instantiation. The host API rejects
-  // the combination before anything is launched.
-  if constexpr (D > 128) {
-    if (dropout) return hipErrorNotSupported;
-  } else if (dropout) {
-    return out_f32 ? launch_all<E, D, MASK, true, true>(st, a, s)
-                   : launch_all<E, D, MASK, true, false>(st, a, s);
-  }
+  if (dropout) return out_f32 ? launch_all<E, D, MASK, true, true>(st, a, s)
+                              : launch_all<E, D, MASK, true, false>(st, a, s);
   return out_f32 ? launch_all<E, D, MASK, false, true>(st, a, s)
                  : launch_all<E, D, MASK, false, false>(st, a, s);
 }

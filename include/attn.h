@@ -91,9 +91,7 @@ typedef enum {
 
 typedef struct {
   int32_t B, H, N, d;      /* batch, heads, sequence length, head dim.
-                              B, H, N >= 1; d in {64, 128, 256}
-                              (the backward has no d = 256 kernel with
-                              dropout: ATTN_ERR_UNSUPPORTED);
+                              B, H, N >= 1; d in {64, 128, 256};
                               N*d and Nk*d must be below 2^31 (per-head
                               index math) and the element counts of every
                               tensor below about 2^62.                     */

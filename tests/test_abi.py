@@ -211,6 +211,5 @@ def test_head_dim_256_is_supported(lib):
     assert _fwd(lib, p, [q, k, v, q, lse]) == 1      # o aliases q: rejected, not unsupported
     bad = _params(d=256, scale=0.0)
     assert _fwd(lib, bad) == 1 and _bwd(lib, bad) == 1
-    drop = _params(d=256, dropout_p=0.1)           # no d = 256 backward with dropout
-    assert _bwd(lib, drop) == 2
-    assert lib.attn_bwd_workspace_bytes(ctypes.byref(drop)) == 0
+    drop = _params(d=256, dropout_p=0.1)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(drop)) > 0
