@@ -142,6 +142,9 @@ def _check_qkv(q, k, v):
             raise ValueError(f"{name} must be a contiguous (B, H, N, d) tensor")
     if not (k.shape == v.shape and q.shape[:2] == k.shape[:2] and q.shape[3] == k.shape[3]):
         raise ValueError("q must be (B, H, N, d) and k, v (B, H, Nk, d)")
+    if k.shape[2] == 0 and q.shape[2] > 0:
+        # Nk = 0 in attn_params means "Nk = N", so zero key rows cannot be passed on.
+        raise ValueError("k and v need at least one row when q has rows")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must have the same dtype")
     if not (q.device == k.device == v.device):
@@ -247,6 +250,9 @@ def dropout_mask(B: int, H: int, N: int, dropout_p: float, seed: int, device,
     torch = _torch()
     lib = load_library()
     nk = N if n_k is None else int(n_k)
+    if nk == 0 and N > 0:
+        # Nk = 0 in attn_params means "Nk = N", so zero key columns cannot be passed on.
+        raise ValueError("n_k must be at least 1 when N > 0")
     keep = torch.empty((B, H, N, nk), dtype=torch.uint8, device=device)
     p = make_params(B, H, N, d, dtype=ATTN_F16, out_dtype=ATTN_F16, scale=1.0,
                     dropout_p=dropout_p, seed=seed, n_k=nk)

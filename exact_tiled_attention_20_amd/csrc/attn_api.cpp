@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int32_t kVersion = 200;  // 0.2.0: Nk and the sliding window
+constexpr int32_t kVersion = 201;  // 0.2.1: empty problems are accepted
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -40,7 +40,7 @@ int32_t key_rows(const attn_params* p) { return p->Nk == 0 ? p->N : p->Nk; }
 // Shape/dtype/scalar checks common to every entry point.
 attn_status check_params(const attn_params* p) {
   if (p == nullptr) return ATTN_ERR_INVALID_ARG;
-  if (p->B < 1 || p->H < 1 || p->N < 1 || p->d < 1) return ATTN_ERR_INVALID_ARG;
+  if (p->B < 0 || p->H < 0 || p->N < 0 || p->d < 1) return ATTN_ERR_INVALID_ARG;
   if (p->Nk < 0 || p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
   if (p->dtype != ATTN_F16 && p->dtype != ATTN_BF16 && p->dtype != ATTN_F32)
     return ATTN_ERR_INVALID_ARG;
@@ -67,6 +67,10 @@ attn_status check_params(const attn_params* p) {
   if (p->d != 64 && p->d != 128 && p->d != 256) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
+
+// A problem with no query rows, heads or batch entries: nothing to compute and
+// no output element to write (call only after check_params has accepted p).
+bool is_empty(const attn_params* p) { return p->B == 0 || p->H == 0 || p->N == 0; }
 
 uint32_t drop_threshold(float p) {
   // floor(p * 2^32) is exact in double for a float p in [0, 1).
@@ -129,6 +133,7 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
                      void* o, float* lse, void* stream) {
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
+  if (is_empty(p)) return ATTN_OK;
   const void* ptrs[] = {q, k, v, o, lse};
   for (const void* x : ptrs)
     if (x == nullptr || !aligned16(x)) return ATTN_ERR_INVALID_ARG;
@@ -186,6 +191,10 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
   if (stage < -1 || stage > 2) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
+  // With no query rows but some keys, dK and dV are (B, H, Nk, d) zeros; no
+  // kernel here writes them.
+  if (is_empty(p))
+    return (p->B > 0 && p->H > 0 && key_rows(p) > 0) ? ATTN_ERR_UNSUPPORTED : ATTN_OK;
   const void* ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
   for (const void* x : ptrs)
     if (x == nullptr || !aligned16(x)) return ATTN_ERR_INVALID_ARG;
@@ -259,6 +268,7 @@ attn_status attn_bwd_stage(const attn_params* p, int32_t stage, const void* q, c
 attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream) {
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
+  if (is_empty(p)) return ATTN_OK;
   if (keep == nullptr || !aligned16(keep)) return ATTN_ERR_INVALID_ARG;
   const double cells = (double)p->B * p->H * p->N * (double)key_rows(p);
   if (cells >= 9.0e15) return ATTN_ERR_INVALID_ARG;

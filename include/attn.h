@@ -91,7 +91,8 @@ typedef enum {
 
 typedef struct {
   int32_t B, H, N, d;      /* batch, heads, sequence length, head dim.
-                              B, H, N >= 1; d in {64, 128, 256};
+                              B, H, N >= 0 (see "Empty problems");
+                              d in {64, 128, 256};
                               N*d and Nk*d must be below 2^31 (per-head
                               index math) and the element counts of every
                               tensor below about 2^62.                     */
@@ -156,6 +157,13 @@ attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream)
 
 /* Static, human-readable text for a status code. */
 const char* attn_status_string(attn_status s);
+
+/* Empty problems.  When B, H or N is 0 (and the other fields are valid),
+ * attn_fwd and attn_dropout_mask return ATTN_OK without reading any pointer
+ * or enqueueing work, and attn_bwd_workspace_bytes returns 0. attn_bwd and
+ * attn_bwd_stage do the same, except for N = 0 with B, H > 0 and Nk > 0:
+ * there dK and dV are all zeros, which no kernel here writes, and they return
+ * ATTN_ERR_UNSUPPORTED. */
 
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t attn_version(void);

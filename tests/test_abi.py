@@ -1,6 +1,7 @@
 """C-ABI tests that need no GPU: the library loads, exports every entry point
-declared in include/attn.h, and rejects every invalid argument on the host
-before anything is enqueued (so these calls never touch a device)."""
+declared in include/attn.h, rejects every invalid argument on the host
+before anything is enqueued, and accepts empty problems without enqueueing
+anything (so these calls never touch a device)."""
 import ctypes
 import os
 import re
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_version() == 200
+    assert lib.attn_version() == 201
     for code, name in attn.STATUS_NAMES.items():
         assert attn.status_string(code).startswith(name)
     assert "unknown" in attn.status_string(99)
@@ -75,7 +76,7 @@ def _params(**kw):
 
 
 INVALID = [
-    dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(B=-1),
+    dict(B=-1), dict(H=-1), dict(N=-1), dict(d=0),
     dict(dtype=7), dict(out_dtype=-1), dict(causal=2),
     dict(scale=0.0), dict(scale=-0.125), dict(scale=float("inf")), dict(scale=float("nan")),
     dict(dropout_p=1.0), dict(dropout_p=-0.1), dict(dropout_p=float("nan")),
@@ -213,3 +214,34 @@ def test_head_dim_256_is_supported(lib):
     assert _fwd(lib, bad) == 1 and _bwd(lib, bad) == 1
     drop = _params(d=256, dropout_p=0.1)
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(drop)) > 0
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(B=0, N=0, H=0),
+                                dict(N=0, causal=True, dropout_p=0.3, window=(5, -1))])
+def test_empty_problem_is_a_no_op(lib, kw):
+    """B, H or N = 0: every entry point accepts the call without reading a
+    pointer (all NULL here) and enqueues nothing (no stream, no device)."""
+    p = _params(**kw)
+    assert _fwd(lib, p, [None] * 5) == 0
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p)) == 0
+    assert _bwd(lib, p, [None] * 10, ws_bytes=0) == 0
+    for stage in (0, 1, 2):
+        assert lib.attn_bwd_stage(ctypes.byref(p), stage, *([None] * 10), 0, None) == 0
+    assert lib.attn_dropout_mask(ctypes.byref(p), None, None) == 0
+
+
+def test_empty_problem_still_validates_the_other_fields(lib):
+    assert _fwd(lib, _params(N=0, scale=0.0), [None] * 5) == 1
+    assert _fwd(lib, _params(B=0, d=96), [None] * 5) == 2
+    assert _bwd(lib, _params(H=0, dropout_p=1.0), [None] * 10, ws_bytes=0) == 1
+    assert lib.attn_dropout_mask(ctypes.byref(_params(N=0, window=(0, -3))), None, None) == 1
+
+
+def test_no_query_rows_with_keys_has_no_backward(lib):
+    """N = 0 with Nk > 0: the forward has nothing to write, but dK and dV would
+    be zeros that no kernel writes, so the backward reports it unsupported."""
+    p = _params(N=0, n_k=50)
+    assert _fwd(lib, p, [None] * 5) == 0
+    assert _bwd(lib, p, [None] * 10, ws_bytes=0) == 2
+    assert lib.attn_bwd_stage(ctypes.byref(p), 1, *([None] * 10), 0, None) == 2
+    assert _bwd(lib, _params(B=0, N=0, n_k=50), [None] * 10, ws_bytes=0) == 0
