@@ -13,10 +13,12 @@ the module raises if the library is missing or a call fails.
     keep = dropout_mask(B, H, N, dropout_p, seed, device, n_k=None)
 
 q and dO are (B, H, N, d); k and v are (B, H, Nk, d) (Nk = N for
-self-attention), contiguous, float16 or bfloat16, d in {64, 128, 256}.
-Query i lines up with key i + Nk - N. window =
-(left, right) keeps keys at most `left` before and `right` after that key
-(-1: unbounded side).
+self-attention; Nk = 0 is allowed: every row then sees no key), contiguous,
+float16 or bfloat16, d in {64, 128, 256}. Every tensor argument, including
+caller-supplied outputs and the workspace, must be on q's device. Query i lines
+up with key i + Nk - N. window = (left, right) keeps keys at most `left` before
+and `right` after that key (-1: unbounded side; sides above 2^31 - 1, wider
+than any sequence, are clamped to it).
 """
 from __future__ import annotations
 
@@ -98,15 +100,24 @@ def status_string(status: int) -> str:
     return load_library().attn_status_string(int(status)).decode()
 
 
+INT32_MAX = (1 << 31) - 1
+
+
 def make_params(B: int, H: int, N: int, d: int, *, dtype: int, out_dtype: int,
                 scale: float, causal: bool = False, kv_len_ptr: int = 0,
-                dropout_p: float = 0.0, seed: int = 0, n_k: int = 0,
+                dropout_p: float = 0.0, seed: int = 0, n_k: Optional[int] = None,
                 window=None) -> AttnParams:
+    """Fill attn_params. n_k defaults to N (self-attention). Window sides above
+    INT32_MAX are clamped to it: the library treats that as wider than any
+    sequence, which is what such a side means (a silent int32 wrap-around
+    would give a different mask)."""
     wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    wl, wr = min(wl, INT32_MAX), min(wr, INT32_MAX)
+    nk = N if n_k is None else int(n_k)
     return AttnParams(int(B), int(H), int(N), int(d), int(dtype), int(out_dtype),
                       float(scale), 1 if causal else 0,
                       ctypes.c_void_p(kv_len_ptr or None), float(dropout_p),
-                      int(seed) & 0xFFFFFFFFFFFFFFFF, int(n_k), wl, wr)
+                      int(seed) & 0xFFFFFFFFFFFFFFFF, nk, wl, wr)
 
 
 # --------------------------------------------------------------------------
@@ -142,9 +153,6 @@ def _check_qkv(q, k, v):
             raise ValueError(f"{name} must be a contiguous (B, H, N, d) tensor")
     if not (k.shape == v.shape and q.shape[:2] == k.shape[:2] and q.shape[3] == k.shape[3]):
         raise ValueError("q must be (B, H, N, d) and k, v (B, H, Nk, d)")
-    if k.shape[2] == 0 and q.shape[2] > 0:
-        # Nk = 0 in attn_params means "Nk = N", so zero key rows cannot be passed on.
-        raise ValueError("k and v need at least one row when q has rows")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must have the same dtype")
     if not (q.device == k.device == v.device):
@@ -165,16 +173,34 @@ def _params_from(q, k, *, causal, kv_len, dropout_p, seed, scale, out_dtype, win
         kv_ptr = kv_len.data_ptr()
     if window is not None and (len(window) != 2 or min(int(w) for w in window) < -1):
         raise ValueError("window must be (left, right) with each side >= -1")
+    # make_params clamps sides above INT32_MAX (wider than any sequence).
     p = make_params(B, H, N, d, dtype=_code(q.dtype), out_dtype=_code(odt), scale=scale,
                     causal=causal, kv_len_ptr=kv_ptr, dropout_p=dropout_p, seed=seed,
                     n_k=k.shape[2], window=window)
     return p, odt
 
 
+def _check_like(name, t, shape, dtype, device):
+    """A tensor argument the kernels read or write: its shape, dtype, device
+    and layout must be exactly what the launch assumes (a wrong-sized or host
+    buffer would be read or written out of bounds on the device)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def fwd(q, k, v, *, causal: bool = False, kv_len=None, dropout_p: float = 0.0,
         seed: int = 0, scale: Optional[float] = None, out_dtype=None, window=None,
         out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """Fused forward: returns (O, lse). O has out_dtype (default q.dtype)."""
+    """Fused forward: returns (O, lse). O has out_dtype (default q.dtype).
+    out and lse, if given, must be a contiguous (B, H, N, d) tensor in out_dtype
+    and a contiguous float32 (B, H, N) tensor on q's device."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
@@ -183,8 +209,12 @@ def fwd(q, k, v, *, causal: bool = False, kv_len=None, dropout_p: float = 0.0,
     B, H, N, d = q.shape
     if out is None:
         out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    else:
+        _check_like("out", out, (B, H, N, d), odt, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_like("lse", lse, (B, H, N), torch.float32, q.device)
     st = lib.attn_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                       out.data_ptr(), lse.data_ptr(), _stream_ptr(q.device))
     if st != 0:
@@ -211,26 +241,24 @@ def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None, dropout_p: fl
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
-    if do.shape != q.shape or do.dtype != q.dtype or not do.is_contiguous():
-        raise ValueError("do must match q in shape and dtype and be contiguous")
+    _check_like("do", do, q.shape, q.dtype, q.device)
     p, odt = _params_from(q, k, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
                           scale=scale, out_dtype=out_dtype, window=window)
-    if o.dtype != odt or o.shape != q.shape or not o.is_contiguous():
-        raise ValueError("o must be the forward output (same out_dtype and shape)")
-    if lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous():
-        raise ValueError("lse must be the forward's float32 (B, H, N) statistic")
+    _check_like("o (the forward output)", o, q.shape, odt, q.device)
+    _check_like("lse (the forward's statistic)", lse, q.shape[:3], torch.float32, q.device)
     need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif not isinstance(workspace, torch.Tensor) or workspace.device != q.device \
+            or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
     if out is None:
         out = (torch.empty(q.shape, dtype=odt, device=q.device),
                torch.empty(k.shape, dtype=odt, device=q.device),
                torch.empty(k.shape, dtype=odt, device=q.device))
     dq, dk, dv = out
-    for t, like in zip(out, (q, k, v)):
-        if t.dtype != odt or t.shape != like.shape or not t.is_contiguous():
-            raise ValueError("gradient outputs must be contiguous, shaped like q, k, v, "
-                             "in out_dtype")
+    for name, t, like in zip(("dq", "dk", "dv"), out, (q, k, v)):
+        _check_like(name, t, like.shape, odt, q.device)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -250,9 +278,6 @@ def dropout_mask(B: int, H: int, N: int, dropout_p: float, seed: int, device,
     torch = _torch()
     lib = load_library()
     nk = N if n_k is None else int(n_k)
-    if nk == 0 and N > 0:
-        # Nk = 0 in attn_params means "Nk = N", so zero key columns cannot be passed on.
-        raise ValueError("n_k must be at least 1 when N > 0")
     keep = torch.empty((B, H, N, nk), dtype=torch.uint8, device=device)
     p = make_params(B, H, N, d, dtype=ATTN_F16, out_dtype=ATTN_F16, scale=1.0,
                     dropout_p=dropout_p, seed=seed, n_k=nk)

@@ -17,7 +17,9 @@
 
 namespace {
 
-constexpr int32_t kVersion = 201;  // 0.2.1: empty problems are accepted
+// 0.3.0: Nk is always explicit (no "0 means N" sentinel); zero key rows and
+// zero query rows are valid problems; pointers of empty tensors may be NULL.
+constexpr int32_t kVersion = 300;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -32,10 +34,18 @@ Range range_of(const void* p, size_t bytes) {
   return Range{a, a + bytes};
 }
 
-bool overlap(Range x, Range y) { return x.lo < y.hi && y.lo < x.hi; }
+// Empty ranges (tensors with no elements) overlap nothing.
+bool overlap(Range x, Range y) {
+  if (x.lo == x.hi || y.lo == y.hi) return false;
+  return x.lo < y.hi && y.lo < x.hi;
+}
 
-// Rows of K and V (0 in the struct means the square case).
-int32_t key_rows(const attn_params* p) { return p->Nk == 0 ? p->N : p->Nk; }
+// Rows of K and V.
+int32_t key_rows(const attn_params* p) { return p->Nk; }
+
+// A tensor pointer is acceptable if it is 16-byte aligned and non-NULL, or if
+// the tensor has no elements (then it is never read or written).
+bool ptr_ok(const void* x, size_t bytes) { return bytes == 0 || (x != nullptr && aligned16(x)); }
 
 // Shape/dtype/scalar checks common to every entry point.
 attn_status check_params(const attn_params* p) {
@@ -134,11 +144,11 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
   if (is_empty(p)) return ATTN_OK;
-  const void* ptrs[] = {q, k, v, o, lse};
-  for (const void* x : ptrs)
-    if (x == nullptr || !aligned16(x)) return ATTN_ERR_INVALID_ARG;
   const size_t in_b = tensor_bytes(p, p->dtype);
   const size_t kin_b = key_tensor_bytes(p, p->dtype);
+  if (!ptr_ok(q, in_b) || !ptr_ok(k, kin_b) || !ptr_ok(v, kin_b) ||
+      !ptr_ok(o, tensor_bytes(p, p->out_dtype)) || !ptr_ok(lse, stat_bytes(p)))
+    return ATTN_ERR_INVALID_ARG;
   const Range outs[] = {range_of(o, tensor_bytes(p, p->out_dtype)), range_of(lse, stat_bytes(p))};
   const Range ins[] = {range_of(q, in_b), range_of(k, kin_b), range_of(v, kin_b)};
   if (overlap(outs[0], outs[1])) return ATTN_ERR_INVALID_ARG;
@@ -191,23 +201,24 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
   if (stage < -1 || stage > 2) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
-  // With no query rows but some keys, dK and dV are (B, H, Nk, d) zeros; no
-  // kernel here writes them.
-  if (is_empty(p))
-    return (p->B > 0 && p->H > 0 && key_rows(p) > 0) ? ATTN_ERR_UNSUPPORTED : ATTN_OK;
-  const void* ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
-  for (const void* x : ptrs)
-    if (x == nullptr || !aligned16(x)) return ATTN_ERR_INVALID_ARG;
-  if (p->kv_len != nullptr && (reinterpret_cast<uintptr_t>(p->kv_len) & 3u))
-    return ATTN_ERR_INVALID_ARG;
-  const size_t need = attn_bwd_workspace_bytes(p);
-  if (workspace == nullptr || workspace_bytes < need ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return ATTN_ERR_WORKSPACE;
+  // Nothing to write: no heads, or neither query nor key rows. With query rows
+  // but no keys, dQ is zero; with keys but no query rows, dK and dV are zero:
+  // both are written by the kernels below.
+  if (p->B == 0 || p->H == 0 || (p->N == 0 && key_rows(p) == 0)) return ATTN_OK;
   const size_t in_b = tensor_bytes(p, p->dtype);
   const size_t out_b = tensor_bytes(p, p->out_dtype);
   const size_t kin_b = key_tensor_bytes(p, p->dtype);
   const size_t kout_b = key_tensor_bytes(p, p->out_dtype);
+  if (!ptr_ok(q, in_b) || !ptr_ok(k, kin_b) || !ptr_ok(v, kin_b) || !ptr_ok(o, out_b) ||
+      !ptr_ok(lse, stat_bytes(p)) || !ptr_ok(d_o, in_b) || !ptr_ok(dq, out_b) ||
+      !ptr_ok(dk, kout_b) || !ptr_ok(dv, kout_b))
+    return ATTN_ERR_INVALID_ARG;
+  if (p->kv_len != nullptr && (reinterpret_cast<uintptr_t>(p->kv_len) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn_bwd_workspace_bytes(p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                   (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return ATTN_ERR_WORKSPACE;
   const Range outs[] = {range_of(dq, out_b), range_of(dk, kout_b), range_of(dv, kout_b),
                         range_of(workspace, need)};
   const Range ins[] = {range_of(q, in_b), range_of(k, kin_b), range_of(v, kin_b),
@@ -268,9 +279,9 @@ attn_status attn_bwd_stage(const attn_params* p, int32_t stage, const void* q, c
 attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream) {
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
-  if (is_empty(p)) return ATTN_OK;
-  if (keep == nullptr || !aligned16(keep)) return ATTN_ERR_INVALID_ARG;
   const double cells = (double)p->B * p->H * p->N * (double)key_rows(p);
+  if (cells == 0.0) return ATTN_OK;
+  if (keep == nullptr || !aligned16(keep)) return ATTN_ERR_INVALID_ARG;
   if (cells >= 9.0e15) return ATTN_ERR_INVALID_ARG;
   attn::MaskArgs a;
   a.keep = keep;

@@ -168,6 +168,9 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
         nqt = last_row < 0 ? 0 : min(nqt, last_row / BQ + 1);
       }
     }
+    // No query row sees these keys (or there are no query rows): dK = dV = 0,
+    // and no copy is issued that the workgroup would never wait for.
+    if (qt0 >= nqt) goto write_out;
     {
       // Wave w's slices of the 256-row K/V block are exactly its own 32 keys.
       TilePairLoader<D, BKW, NW> kvload;
@@ -326,6 +329,7 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     }
   }
 
+write_out:
   // Write dK (times scale) and dV: lane holds column 32db + l32 of key rows
   // kw + 8(r/4) + 4hh + r%4.
 #pragma unroll
@@ -566,8 +570,11 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
 
 template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
+  // A kernel with no work item is not launched (a zero-sized grid is a launch
+  // error): no query rows leave only dK = dV = 0 to write, no key rows only
+  // dQ = 0.
   hipError_t e = hipSuccess;
-  if (stage < 0 || stage == 0) {
+  if ((stage < 0 || stage == 0) && a.N > 0) {
     const long long rows = (long long)a.B * a.H * a.N;
     const long long threads = rows * (D / 8);
     hipLaunchKernelGGL((attn_bwd_preprocess_kernel<E, D, OUT_F32>),
@@ -575,7 +582,7 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stage < 0 || stage == 1) {
+  if ((stage < 0 || stage == 1) && a.Nk > 0) {
     constexpr int NW = dkdv_waves<D>();
     const int nkb = (a.Nk + 32 * NW - 1) / (32 * NW);
     const int tk = a.B * a.H * nkb;
@@ -584,7 +591,7 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stage < 0 || stage == 2) {
+  if ((stage < 0 || stage == 2) && a.N > 0) {
     const int nqb = (a.N + 127) / 128;
     const int tq = a.B * a.H * nqb;
     hipLaunchKernelGGL((attn_bwd_dq_kernel<E, D, MASK, DROPOUT, OUT_F32>),

@@ -8,8 +8,8 @@
 // the page's separate l and m). Mask and dropout are fused into the same pass
 // (anthology-of-the-sota SOTA-114, "The general form of the practice above
 // it"); the sequence-dimension split of work across workgroups follows the
-// same page's note on FlashAttention-2 ("Why this only works as a fused
-// kernel").
+// note on FlashAttention-2 in "Why FlashAttention Is a Kernel Story", section
+// "Why this only works as a fused kernel".
 //
 // Mapping to CDNA4:
 //   * One workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32

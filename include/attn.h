@@ -29,8 +29,9 @@
  * Conventions shared by every entry point
  *   Layout.  Q, O, dO, dQ are dense row-major (B, H, N, d) arrays: element
  *            (b, h, i, c) sits at ((b*H + h)*N + i)*d + c. K, V, dK, dV are
- *            (B, H, Nk, d) in the same layout, Nk = N unless set (cross-
- *            attention with a non-square grid). lse and the backward's D are
+ *            (B, H, Nk, d) in the same layout (Nk = N for self-attention,
+ *            Nk != N for cross-attention on a non-square grid). lse and the
+ *            backward's D are
  *            (B, H, N) float32.
  *   Masks.   Query i lines up with key c_i = i + Nk - N (the last query with
  *            the last key; c_i = i when Nk = N). Every set mask must keep a
@@ -54,9 +55,11 @@
  *            1 / (1 - p). The log-sum-exp is over the undropped scores.
  *            (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3".)
  *   Memory.  All tensor pointers are device pointers owned by the caller and
- *            must be 16-byte aligned. Outputs must not alias inputs. The
- *            library never allocates, frees or synchronises; it keeps no
- *            global state, so calls from several host threads are safe.
+ *            must be 16-byte aligned; the pointer of a tensor with no elements
+ *            may be NULL (it is never read or written). Outputs must not alias
+ *            inputs. The library never allocates, frees or synchronises; it
+ *            keeps no global state, so calls from several host threads are
+ *            safe.
  *   Streams. `stream` is a hipStream_t (NULL = the default stream). Work is
  *            enqueued asynchronously; faults inside a kernel surface at the
  *            caller's next synchronisation.
@@ -103,26 +106,42 @@ typedef struct {
   const int32_t* kv_len;   /* device int32[B] of valid key counts, or NULL */
   float dropout_p;         /* 0 <= p < 1; 0 disables dropout               */
   uint64_t seed;           /* Philox key for dropout                       */
-  int32_t Nk;              /* rows of K, V, dK, dV; 0 means Nk = N; >= 0   */
+  int32_t Nk;              /* rows of K, V, dK, dV (>= 0); Nk = N for
+                              self-attention. Always explicit: Nk = 0 means
+                              no keys (every row sees none).               */
   int32_t window_left;     /* sliding window, keys before c_i; -1 = none   */
   int32_t window_right;    /* sliding window, keys after c_i;  -1 = none   */
 } attn_params;
 
 /* Forward: O (out_dtype, (B,H,N,d)) and lse (float32, (B,H,N)), where
  * lse_i = log sum_j exp(scale * Q_i . K_j) over the visible keys. K and V are
- * (B,H,Nk,d). */
+ * (B,H,Nk,d). Reads Q, K, V once per query block; writes only O and lse.
+ * ("Why FlashAttention Is a Kernel Story", section "Tiling: fitting the work
+ * inside SRAM": per-block running max and denominator, rescaled O, final
+ * O / l; the single log-sum-exp replaces the page's separate l and m.
+ * SOTA-114, "The general form of the practice above it": scale, mask,
+ * softmax and dropout fused between the two products.) */
 attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
                      const void* v, void* o, float* lse, void* stream);
 
-/* Size in bytes of the workspace attn_bwd needs for these parameters
- * (0 if the parameters are invalid). */
+/* Size in bytes of the workspace attn_bwd needs for these parameters:
+ * two float32 (B,H,N) arrays (D_i = dO_i . O_i and lse_i * log2(e)), each
+ * rounded up to 256 bytes; 0 if the parameters are invalid or N = 0.
+ * (The backward's row statistics: "Why FlashAttention Is a Kernel Story",
+ * section "When it falls down", recomputation from the stored output and
+ * log-sum-exp.) */
 size_t attn_bwd_workspace_bytes(const attn_params* p);
 
 /* Backward: given Q, K, V, the forward's O (out_dtype) and lse, and dO
  * (dtype), writes dQ (B,H,N,d), dK and dV (B,H,Nk,d), all in out_dtype.
- * Scores and probabilities are recomputed from lse; nothing N x Nk is stored. `workspace` is a device
- * buffer of at least attn_bwd_workspace_bytes(p) bytes, owned by the caller,
- * 256-byte aligned; its contents on entry do not matter. */
+ * Scores and probabilities are recomputed from lse; nothing N x Nk is stored.
+ * `workspace` is a device buffer of at least attn_bwd_workspace_bytes(p)
+ * bytes, owned by the caller, 256-byte aligned (NULL when that size is 0);
+ * its contents on entry do not matter. With N = 0 it writes dK = dV = 0;
+ * with Nk = 0 it writes dQ = 0.
+ * ("Why FlashAttention Is a Kernel Story", section "When it falls down",
+ * backward pass: S and P are rebuilt from Q, K and the saved log-sum-exp
+ * rather than read back from memory.) */
 attn_status attn_bwd(const attn_params* p, const void* q, const void* k,
                      const void* v, const void* o, const float* lse,
                      const void* d_o, void* dq, void* dk, void* dv,
@@ -152,20 +171,23 @@ attn_status attn_bwd_stage(const attn_params* p, int32_t stage, const void* q,
 /* Test aid: writes the dropout keep-mask keep[b][h][i][j] (uint8 0/1, device,
  * (B,H,N,Nk)) that attn_fwd and attn_bwd use for these parameters. Masking by
  * causal/window/kv_len is not applied here: it is the raw Philox keep
- * decision. */
+ * decision. (SOTA-114, "The general form of the practice above it": dropout
+ * is one of the fused steps; the generator is Philox4x32-10 from Salmon et
+ * al., SC'11, keyed as described under "Dropout" above.) */
 attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream);
 
-/* Static, human-readable text for a status code. */
+/* Static, human-readable text for a status code. (SOTA-114, "Cost": an
+ * unsupported combination is reported, never served by a slower path.) */
 const char* attn_status_string(attn_status s);
 
 /* Empty problems.  When B, H or N is 0 (and the other fields are valid),
- * attn_fwd and attn_dropout_mask return ATTN_OK without reading any pointer
- * or enqueueing work, and attn_bwd_workspace_bytes returns 0. attn_bwd and
- * attn_bwd_stage do the same, except for N = 0 with B, H > 0 and Nk > 0:
- * there dK and dV are all zeros, which no kernel here writes, and they return
- * ATTN_ERR_UNSUPPORTED. */
+ * attn_fwd returns ATTN_OK without reading any pointer or enqueueing work;
+ * so does attn_dropout_mask when B*H*N*Nk is 0, and attn_bwd_workspace_bytes
+ * returns 0. attn_bwd and attn_bwd_stage do nothing when B or H is 0 or when
+ * N = Nk = 0; with N = 0 and Nk > 0 they write dK = dV = 0, and with Nk = 0
+ * and N > 0 they write dQ = 0 (each row sees no key: O = 0, lse = -inf). */
 
-/* Library version as major*10000 + minor*100 + patch. */
+/* Library version as major*10000 + minor*100 + patch (0.3.0: Nk explicit). */
 int32_t attn_version(void);
 
 #ifdef __cplusplus

@@ -1,0 +1,212 @@
+// Host-only driver for the C ABI's validation layer (attn_api.cpp), built with
+// g++ under AddressSanitizer and UndefinedBehaviorSanitizer by
+// tests/test_host_sanitize.py. The kernel launchers are replaced by stubs that
+// record the launch descriptor and never touch a device, so every path -- the
+// rejections and the argument marshalling up to the launch -- runs on the CPU.
+// Pointers are fake, 16-byte-aligned addresses that are never dereferenced.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/attn.h"
+#include "../../exact_tiled_attention_20_amd/csrc/kernels.hpp"
+
+namespace attn {
+static int g_fwd_calls = 0, g_bwd_calls = 0, g_mask_calls = 0;
+static FwdArgs g_fwd;
+static BwdArgs g_bwd;
+static int g_mask_mode = -1, g_stage = -9;
+
+hipError_t launch_fwd(int, int, int mask, bool, bool, const FwdArgs& a, hipStream_t) {
+  ++g_fwd_calls;
+  g_fwd = a;
+  g_mask_mode = mask;
+  return hipSuccess;
+}
+hipError_t launch_bwd(int, int, int mask, bool, bool, int stage, const BwdArgs& a,
+                      hipStream_t) {
+  ++g_bwd_calls;
+  g_bwd = a;
+  g_mask_mode = mask;
+  g_stage = stage;
+  return hipSuccess;
+}
+hipError_t launch_dropout_mask(const MaskArgs&, hipStream_t) {
+  ++g_mask_calls;
+  return hipSuccess;
+}
+}  // namespace attn
+
+static int g_failures = 0;
+#define CHECK(cond)                                                      \
+  do {                                                                   \
+    if (!(cond)) {                                                       \
+      std::fprintf(stderr, "FAILED line %d: %s\n", __LINE__, #cond);     \
+      ++g_failures;                                                      \
+    }                                                                    \
+  } while (0)
+
+static void* fake(int i) { return reinterpret_cast<void*>((uintptr_t)0x10000 + ((uintptr_t)i << 40)); }
+
+static attn_params base() {
+  attn_params p{};
+  p.B = 2;
+  p.H = 3;
+  p.N = 100;
+  p.d = 64;
+  p.dtype = ATTN_F16;
+  p.out_dtype = ATTN_F16;
+  p.scale = 0.125f;
+  p.causal = 0;
+  p.kv_len = nullptr;
+  p.dropout_p = 0.f;
+  p.seed = 1;
+  p.Nk = 100;
+  p.window_left = -1;
+  p.window_right = -1;
+  return p;
+}
+
+static attn_status fwd(const attn_params& p) {
+  return attn_fwd(&p, fake(0), fake(1), fake(2), fake(3), (float*)fake(4), nullptr);
+}
+static attn_status bwd(const attn_params& p, size_t ws = (size_t)1 << 30, int stage = -1) {
+  if (stage < 0)
+    return attn_bwd(&p, fake(0), fake(1), fake(2), fake(3), (const float*)fake(4), fake(5),
+                    fake(6), fake(7), fake(8), fake(9), ws, nullptr);
+  return attn_bwd_stage(&p, stage, fake(0), fake(1), fake(2), fake(3), (const float*)fake(4),
+                        fake(5), fake(6), fake(7), fake(8), fake(9), ws, nullptr);
+}
+
+int main() {
+  using namespace attn;
+  // Version and status strings.
+  CHECK(attn_version() == 300);
+  for (int s = 0; s <= 5; ++s) CHECK(attn_status_string((attn_status)s) != nullptr);
+
+  // Invalid fields: nothing is launched.
+  {
+    attn_params bad[12];
+    for (auto& b : bad) b = base();
+    bad[0].B = -1;
+    bad[1].d = 0;
+    bad[2].dtype = 9;
+    bad[3].causal = 2;
+    bad[4].scale = 0.f;
+    bad[5].dropout_p = 1.f;
+    bad[6].Nk = -1;
+    bad[7].window_left = -2;
+    bad[8].N = 1 << 24;
+    bad[8].d = 128;
+    bad[9].B = 1 << 16;
+    bad[9].H = 1 << 15;
+    bad[10].scale = __builtin_nanf("");
+    bad[11].window_right = -5;
+    for (auto& b : bad) {
+      CHECK(fwd(b) == ATTN_ERR_INVALID_ARG);
+      CHECK(bwd(b) == ATTN_ERR_INVALID_ARG);
+      CHECK(attn_bwd_workspace_bytes(&b) == 0);
+      CHECK(attn_dropout_mask(&b, (uint8_t*)fake(0), nullptr) == ATTN_ERR_INVALID_ARG);
+    }
+    CHECK(attn_fwd(nullptr, fake(0), fake(1), fake(2), fake(3), (float*)fake(4), nullptr) ==
+          ATTN_ERR_INVALID_ARG);
+    CHECK(g_fwd_calls == 0 && g_bwd_calls == 0 && g_mask_calls == 0);
+  }
+  // Unsupported combinations.
+  {
+    attn_params p = base();
+    p.d = 96;
+    CHECK(fwd(p) == ATTN_ERR_UNSUPPORTED);
+    p = base();
+    p.out_dtype = ATTN_BF16;
+    CHECK(bwd(p) == ATTN_ERR_UNSUPPORTED);
+    CHECK(g_fwd_calls == 0 && g_bwd_calls == 0);
+  }
+  // Pointer checks.
+  {
+    attn_params p = base();
+    CHECK(attn_fwd(&p, nullptr, fake(1), fake(2), fake(3), (float*)fake(4), nullptr) ==
+          ATTN_ERR_INVALID_ARG);
+    CHECK(attn_fwd(&p, (char*)fake(0) + 8, fake(1), fake(2), fake(3), (float*)fake(4),
+                   nullptr) == ATTN_ERR_INVALID_ARG);
+    CHECK(attn_fwd(&p, fake(0), fake(1), fake(2), fake(0), (float*)fake(4), nullptr) ==
+          ATTN_ERR_INVALID_ARG);  // o aliases q
+    const size_t need = attn_bwd_workspace_bytes(&p);
+    CHECK(need == 2 * ((2 * 3 * 100 * 4 + 255) / 256 * 256));
+    CHECK(bwd(p, need - 1) == ATTN_ERR_WORKSPACE);
+    CHECK(g_fwd_calls == 0 && g_bwd_calls == 0);
+  }
+  // Valid calls reach the launcher with the descriptor filled in.
+  {
+    attn_params p = base();
+    p.causal = 1;
+    CHECK(fwd(p) == ATTN_OK);
+    CHECK(g_fwd_calls == 1 && g_mask_mode == kMaskCausal);
+    CHECK(g_fwd.N == 100 && g_fwd.Nk == 100 && g_fwd.nqb == 1 && g_fwd.total == 6);
+    CHECK(g_fwd.per_xcd == 1 && g_fwd.band_hi == 0);
+    p = base();
+    p.Nk = 300;
+    p.causal = 1;
+    p.window_left = 7;
+    p.dropout_p = 0.1f;
+    CHECK(fwd(p) == ATTN_OK);
+    CHECK(g_mask_mode == kMaskBand && g_fwd.band_hi == 200 && g_fwd.band_lo == 193);
+    CHECK(g_fwd.drop_threshold == 429496736u);
+    p.seed = 0x0123456789ABCDEFull;
+    CHECK(bwd(p) == ATTN_OK && g_stage == -1);
+    CHECK(g_bwd.seed_lo == 0x89ABCDEFu && g_bwd.seed_hi == 0x01234567u);
+    CHECK(g_bwd.delta == (float*)fake(9));
+    CHECK((char*)g_bwd.lse2 == (char*)fake(9) + (2 * 3 * 100 * 4 + 255) / 256 * 256);
+    for (int st = 0; st < 3; ++st) CHECK(bwd(p, (size_t)1 << 30, st) == ATTN_OK && g_stage == st);
+    CHECK(bwd(p, (size_t)1 << 30, 3) == ATTN_ERR_INVALID_ARG);
+    // Huge window sides are clamped inside the band arithmetic.
+    p = base();
+    p.window_left = 0x7FFFFFFF;
+    p.window_right = 0x7FFFFFFF;
+    CHECK(fwd(p) == ATTN_OK && g_mask_mode == kMaskBand);
+    CHECK(g_fwd.band_lo == -kBandInf && g_fwd.band_hi == kBandInf);
+  }
+  // Empty problems and empty tensors.
+  {
+    const int launches = g_fwd_calls + g_bwd_calls + g_mask_calls;
+    attn_params p = base();
+    p.N = 0;
+    p.Nk = 0;
+    CHECK(attn_fwd(&p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == ATTN_OK);
+    CHECK(attn_bwd(&p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                   nullptr, nullptr, 0, nullptr) == ATTN_OK);
+    CHECK(attn_dropout_mask(&p, nullptr, nullptr) == ATTN_OK);
+    p = base();
+    p.B = 0;
+    CHECK(bwd(p) == ATTN_OK);
+    CHECK(g_fwd_calls + g_bwd_calls + g_mask_calls == launches);
+    // N = 0 with keys: the backward still runs (dK = dV = 0); the query-side
+    // tensors may be NULL, the workspace is not needed.
+    p = base();
+    p.N = 0;
+    p.Nk = 40;
+    CHECK(attn_bwd_workspace_bytes(&p) == 0);
+    CHECK(attn_bwd(&p, nullptr, fake(1), fake(2), nullptr, nullptr, nullptr, nullptr, fake(7),
+                   fake(8), nullptr, 0, nullptr) == ATTN_OK);
+    CHECK(g_bwd.N == 0 && g_bwd.Nk == 40);
+    CHECK(attn_bwd(&p, nullptr, nullptr, fake(2), nullptr, nullptr, nullptr, nullptr, fake(7),
+                   fake(8), nullptr, 0, nullptr) == ATTN_ERR_INVALID_ARG);
+    // Nk = 0 with query rows: K, V, dK, dV may be NULL.
+    p = base();
+    p.Nk = 0;
+    CHECK(attn_fwd(&p, fake(0), nullptr, nullptr, fake(3), (float*)fake(4), nullptr) == ATTN_OK);
+    CHECK(g_fwd.Nk == 0);
+    CHECK(attn_bwd(&p, fake(0), nullptr, nullptr, fake(3), (const float*)fake(4), fake(5),
+                   fake(6), nullptr, nullptr, fake(9), (size_t)1 << 20, nullptr) == ATTN_OK);
+    CHECK(attn_dropout_mask(&p, nullptr, nullptr) == ATTN_OK);
+    // An empty tensor's pointer inside another tensor is not aliasing.
+    CHECK(attn_fwd(&p, fake(0), (char*)fake(0) + 64, (char*)fake(0) + 64, fake(3),
+                   (float*)fake(4), nullptr) == ATTN_OK);
+  }
+  if (g_failures) {
+    std::fprintf(stderr, "%d check(s) failed\n", g_failures);
+    return 1;
+  }
+  std::printf("abi host checks OK\n");
+  return 0;
+}

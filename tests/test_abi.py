@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_version() == 201
+    assert lib.attn_version() == 300
     for code, name in attn.STATUS_NAMES.items():
         assert attn.status_string(code).startswith(name)
     assert "unknown" in attn.status_string(99)
@@ -237,11 +237,46 @@ def test_empty_problem_still_validates_the_other_fields(lib):
     assert lib.attn_dropout_mask(ctypes.byref(_params(N=0, window=(0, -3))), None, None) == 1
 
 
-def test_no_query_rows_with_keys_has_no_backward(lib):
-    """N = 0 with Nk > 0: the forward has nothing to write, but dK and dV would
-    be zeros that no kernel writes, so the backward reports it unsupported."""
+def test_no_query_rows_with_keys_needs_the_key_tensors(lib):
+    """N = 0 with Nk > 0: the forward has nothing to write; the backward writes
+    dK = dV = 0, so the (non-empty) key tensors need real pointers. With NULL
+    ones it is rejected before anything is enqueued."""
     p = _params(N=0, n_k=50)
     assert _fwd(lib, p, [None] * 5) == 0
-    assert _bwd(lib, p, [None] * 10, ws_bytes=0) == 2
-    assert lib.attn_bwd_stage(ctypes.byref(p), 1, *([None] * 10), 0, None) == 2
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p)) == 0
+    assert _bwd(lib, p, [None] * 10, ws_bytes=0) == 1
+    assert lib.attn_bwd_stage(ctypes.byref(p), 1, *([None] * 10), 0, None) == 1
     assert _bwd(lib, _params(B=0, N=0, n_k=50), [None] * 10, ws_bytes=0) == 0
+
+
+def test_zero_key_rows_need_only_the_query_side(lib):
+    """Nk = 0 with N > 0 is a valid problem (every row sees no key). The key
+    tensors are empty, so their pointers may be NULL, but the query-side ones
+    may not (checked here with NULL q, which fails before any launch)."""
+    p = _params(N=40, n_k=0)
+    q, k, v, o, lse = _ptrs(5)
+    assert _fwd(lib, p, [None, None, None, o, lse]) == 1
+    ptrs = _ptrs(10)
+    for slot in (0, 1, 2, 7, 8):            # q, and the empty k, v, dk, dv
+        ptrs[slot] = None
+    assert _bwd(lib, p, ptrs, ws_bytes=1 << 20) == 1
+    assert lib.attn_dropout_mask(ctypes.byref(p), None, None) == 0   # no cells
+
+
+def test_empty_ranges_do_not_alias(lib):
+    """A tensor with no elements overlaps nothing, even where its (unused)
+    pointer falls inside another tensor. Checked on a problem that fails later
+    for a reason the aliasing check cannot hide: d = 96 is reported as
+    unsupported, not as invalid."""
+    p = _params(N=40, n_k=0, d=96)
+    q, k, v, o, lse = _ptrs(5)
+    assert _fwd(lib, p, [q, q + 64, q + 64, o, lse]) == 2
+
+
+def test_window_sides_beyond_int32_are_clamped():
+    p = attn.make_params(1, 1, 8, 64, dtype=attn.ATTN_F16, out_dtype=attn.ATTN_F16,
+                         scale=0.125, window=(2 ** 32 + 5, 2 ** 40))
+    assert p.window_left == 2 ** 31 - 1 and p.window_right == 2 ** 31 - 1
+    p = attn.make_params(1, 1, 8, 64, dtype=attn.ATTN_F16, out_dtype=attn.ATTN_F16,
+                         scale=0.125, window=(3, -1))
+    assert (p.window_left, p.window_right, p.Nk) == (3, -1, 8)

@@ -1,8 +1,10 @@
-"""Empty problems through the torch binding on the device: B, H or N = 0 give
-empty outputs and enqueue no kernel, and zero key rows against a non-empty
-query block is refused before the library is called (Nk = 0 in the C struct
-stands for Nk = N, so passing it on would make the kernels read N rows of an
-empty K)."""
+"""Empty and degenerate problems through the torch binding on the device.
+
+B, H or N = 0 give empty outputs and enqueue no kernel. Zero key rows against
+a non-empty query block (Nk = 0) is a valid problem: every row sees no key, so
+O = 0, lse = -inf and dQ = 0. Zero query rows against keys (N = 0) leave
+dK = dV = 0 to write. The outputs are filled with NaN first, so a zero that
+was never written would show."""
 import pytest
 import torch
 
@@ -26,6 +28,10 @@ def _qkv(B, H, N, Nk, d=64, dt=torch.float16):
     return mk(N), mk(Nk), mk(Nk)
 
 
+def _nan_like(t, dtype=None):
+    return torch.full(t.shape, float("nan"), dtype=dtype or t.dtype, device=t.device)
+
+
 @pytest.mark.parametrize("B,H,N", [(0, 3, 100), (2, 0, 100), (2, 3, 0), (0, 0, 0)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_empty_forward_and_backward(B, H, N, causal):
@@ -40,17 +46,83 @@ def test_empty_forward_and_backward(B, H, N, causal):
     torch.cuda.synchronize()
 
 
-def test_no_query_rows_with_keys():
-    q, k, v = _qkv(2, 3, 0, 40)
-    o, lse = attn.fwd(q, k, v)
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_no_query_rows_with_keys(d, causal):
+    """N = 0, Nk = 40: nothing to compute forward; the backward writes
+    dK = dV = 0 (no query sees the keys)."""
+    q, k, v = _qkv(2, 3, 0, 40, d=d)
+    o, lse = attn.fwd(q, k, v, causal=causal)
     assert o.numel() == 0 and lse.numel() == 0
-    with pytest.raises(attn.AttnError):
-        attn.bwd(q, k, v, o, lse, torch.zeros_like(q))
+    out = (torch.empty_like(q), _nan_like(k), _nan_like(v))
+    dq, dk, dv = attn.bwd(q, k, v, o, lse, torch.zeros_like(q), causal=causal, out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dv).item() == 0
+    assert not torch.isnan(dk).any() and not torch.isnan(dv).any()
 
 
-def test_zero_key_rows_with_queries_is_refused():
-    q, k, v = _qkv(2, 3, 50, 0)
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("out_dtype", [None, torch.float32])
+def test_zero_key_rows_with_queries(d, out_dtype):
+    """Nk = 0, N = 50: every row sees no key: O = 0, lse = -inf, dQ = 0, and
+    the dropout mask has no cells."""
+    q, k, v = _qkv(2, 3, 50, 0, d=d)
+    odt = q.dtype if out_dtype is None else out_dtype
+    o, lse = attn.fwd(q, k, v, out_dtype=out_dtype, dropout_p=0.1, seed=4,
+                      out=_nan_like(q, odt), lse=_nan_like(q[..., 0], torch.float32))
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(6)).to(q.dtype).to(DEV)
+    out = (_nan_like(q, odt), torch.empty(k.shape, dtype=odt, device=DEV),
+           torch.empty(v.shape, dtype=odt, device=DEV))
+    dq, dk, dv = attn.bwd(q, k, v, o, lse, do, out_dtype=out_dtype, dropout_p=0.1, seed=4,
+                          out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0 and not torch.isnan(o).any()
+    assert torch.isneginf(lse).all()
+    assert torch.count_nonzero(dq).item() == 0 and not torch.isnan(dq).any()
+    assert dk.numel() == 0 and dv.numel() == 0
+    keep = attn.dropout_mask(2, 3, 50, 0.1, 1, DEV, n_k=0)
+    assert keep.shape == (2, 3, 50, 0)
+
+
+def test_binding_rejects_bad_tensors_before_any_launch():
+    """Caller-supplied outputs, lse, dO and the workspace are checked for shape,
+    dtype, device and layout: a wrong one raises ValueError and nothing runs."""
+    q, k, v = _qkv(1, 2, 96, 96)
+    o, lse = attn.fwd(q, k, v)
+    do = torch.zeros_like(q)
+    bad_outs = [
+        dict(out=torch.empty(1, 2, 95, 64, dtype=q.dtype, device=DEV)),       # too small
+        dict(out=torch.empty_like(q, dtype=torch.float32)),                   # wrong dtype
+        dict(out=torch.empty(q.shape, dtype=q.dtype)),                        # host memory
+        dict(out=torch.empty(1, 2, 64, 96, dtype=q.dtype, device=DEV).transpose(2, 3)),
+        dict(lse=torch.empty(1, 2, 96, dtype=torch.float16, device=DEV)),
+        dict(lse=torch.empty(1, 2, 96)),
+    ]
+    for kw in bad_outs:
+        with pytest.raises(ValueError):
+            attn.fwd(q, k, v, **kw)
     with pytest.raises(ValueError):
-        attn.fwd(q, k, v)
+        attn.bwd(q, k, v, o, lse, do.cpu())
     with pytest.raises(ValueError):
-        attn.dropout_mask(2, 3, 50, 0.1, 1, DEV, n_k=0)
+        attn.bwd(q, k, v, o.cpu(), lse, do)
+    with pytest.raises(ValueError):
+        attn.bwd(q, k, v, o, lse.cpu(), do)
+    with pytest.raises(ValueError):
+        attn.bwd(q, k, v, o, lse, do, workspace=torch.empty(1 << 16, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        attn.bwd(q, k, v, o, lse, do,
+                 out=(torch.empty_like(q), torch.empty_like(k).cpu(), torch.empty_like(v)))
+    with pytest.raises(ValueError):
+        attn.bwd(q, k, v, o, lse, do,
+                 out=(torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)[:, :, :-1]))
+    torch.cuda.synchronize()
+
+
+def test_huge_window_sides_equal_the_unbounded_window():
+    """Window sides beyond int32 are clamped to 2^31 - 1 (wider than any
+    sequence), which gives the unwindowed result, not a wrapped-around one."""
+    q, k, v = _qkv(1, 2, 130, 130)
+    o_ref, l_ref = attn.fwd(q, k, v, causal=True)
+    o, l = attn.fwd(q, k, v, causal=True, window=(2 ** 32 + 5, 2 ** 40))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
