@@ -10,6 +10,7 @@ the module raises if the library is missing or a call fails.
     o, lse = fwd(q, k, v, causal=False, kv_len=None, dropout_p=0.0, seed=0,
                  scale=None, out_dtype=None, window=None)
     dq, dk, dv = bwd(q, k, v, o, lse, do, <same keyword arguments>)
+    dq, dk, dv = bwd_noalloc(q, k, v, o, lse, do, <same keyword arguments>)
     keep = dropout_mask(B, H, N, dropout_p, seed, device, n_k=None)
 
 q and dO are (B, H, N, d); k and v are (B, H, Nk, d) (Nk = N for
@@ -32,10 +33,11 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_F16, ATTN_BF16, ATTN_F32 = 0, 1, 2
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
-                3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_LAUNCH"}
+                3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_LAUNCH", 5: "ATTN_ERR_TOO_LARGE"}
 
 # Entry points declared in include/attn.h (checked by the ABI tests).
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
+           "attn_bwd_noalloc", "attn_bwd_noalloc_max_workspace_bytes",
            "attn_dropout_mask", "attn_status_string", "attn_version")
 BWD_STAGE_PREPROCESS, BWD_STAGE_DKDV, BWD_STAGE_DQ = 0, 1, 2
 
@@ -84,6 +86,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_stage.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
     lib.attn_bwd_stage.restype = ctypes.c_int
+    lib.attn_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
+    lib.attn_bwd_noalloc_max_workspace_bytes.argtypes = []
+    lib.attn_bwd_noalloc_max_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [P]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_dropout_mask.argtypes = [P, vp, vp]
@@ -270,6 +276,41 @@ def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None, dropout_p: fl
     if st != 0:
         raise AttnError(st, "attn_bwd" if stage is None else "attn_bwd_stage")
     return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, do, *, causal: bool = False, kv_len=None,
+                dropout_p: float = 0.0, seed: int = 0, scale: Optional[float] = None,
+                out_dtype=None, window=None, out=None):
+    """attn_bwd_noalloc: the backward with the library's fixed per-GPU scratch
+    in place of a workspace (bit-identical to bwd). The library allocates
+    nothing; pass `out` = (dq, dk, dv) to allocate nothing here either.
+    Problems whose workspace would exceed the scratch raise AttnError
+    (ATTN_ERR_TOO_LARGE)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    _check_like("do", do, q.shape, q.dtype, q.device)
+    p, odt = _params_from(q, k, causal=causal, kv_len=kv_len, dropout_p=dropout_p, seed=seed,
+                          scale=scale, out_dtype=out_dtype, window=window)
+    _check_like("o (the forward output)", o, q.shape, odt, q.device)
+    _check_like("lse (the forward's statistic)", lse, q.shape[:3], torch.float32, q.device)
+    if out is None:
+        out = (torch.empty(q.shape, dtype=odt, device=q.device),
+               torch.empty(k.shape, dtype=odt, device=q.device),
+               torch.empty(k.shape, dtype=odt, device=q.device))
+    dq, dk, dv = out
+    for name, t, like in zip(("dq", "dk", "dv"), out, (q, k, v)):
+        _check_like(name, t, like.shape, odt, q.device)
+    st = lib.attn_bwd_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), _stream_ptr(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_noalloc")
+    return dq, dk, dv
+
+
+def noalloc_max_workspace_bytes() -> int:
+    return int(load_library().attn_bwd_noalloc_max_workspace_bytes())
 
 
 def dropout_mask(B: int, H: int, N: int, dropout_p: float, seed: int, device,

@@ -13,6 +13,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "api_internal.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -133,6 +134,9 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: no kernel for this head dimension / dtype combination";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: backward workspace missing, misaligned or too small";
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case ATTN_ERR_TOO_LARGE:
+      return "ATTN_ERR_TOO_LARGE: the problem needs more than the fixed scratch of the "
+             "no-allocation entry point (use attn_bwd with a workspace)";
   }
   return "unknown attn_status";
 }
@@ -194,10 +198,12 @@ size_t attn_bwd_workspace_bytes(const attn_params* p) {
   return 2 * ((stat_bytes(p) + 255) & ~size_t(255));
 }
 
+// validate_only: run every check except those on the workspace, then return
+// without any HIP call.
 static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, const void* k,
                             const void* v, const void* o, const float* lse, const void* d_o,
                             void* dq, void* dk, void* dv, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, bool validate_only = false) {
   if (stage < -1 || stage > 2) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
@@ -215,7 +221,7 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
     return ATTN_ERR_INVALID_ARG;
   if (p->kv_len != nullptr && (reinterpret_cast<uintptr_t>(p->kv_len) & 3u))
     return ATTN_ERR_INVALID_ARG;
-  const size_t need = attn_bwd_workspace_bytes(p);
+  const size_t need = validate_only ? 0 : attn_bwd_workspace_bytes(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
                    (reinterpret_cast<uintptr_t>(workspace) & 255u)))
     return ATTN_ERR_WORKSPACE;
@@ -229,6 +235,7 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
     for (const Range& x : ins)
       if (overlap(outs[i], x)) return ATTN_ERR_INVALID_ARG;
   }
+  if (validate_only) return ATTN_OK;
 
   attn::BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -275,6 +282,20 @@ attn_status attn_bwd_stage(const attn_params* p, int32_t stage, const void* q, c
   if (stage < ATTN_BWD_STAGE_PREPROCESS || stage > ATTN_BWD_STAGE_DQ) return ATTN_ERR_INVALID_ARG;
   return bwd_impl(p, stage, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes, stream);
 }
+
+}  // extern "C"
+
+namespace attn {
+
+attn_status bwd_validate_without_workspace(const attn_params* p, const void* q, const void* k,
+                                           const void* v, const void* o, const float* lse,
+                                           const void* d_o, void* dq, void* dk, void* dv) {
+  return bwd_impl(p, -1, q, k, v, o, lse, d_o, dq, dk, dv, nullptr, 0, nullptr, true);
+}
+
+}  // namespace attn
+
+extern "C" {
 
 attn_status attn_dropout_mask(const attn_params* p, uint8_t* keep, void* stream) {
   attn_status st = check_params(p);

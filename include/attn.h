@@ -89,7 +89,8 @@ typedef enum {
   ATTN_ERR_INVALID_ARG = 1,  /* NULL/misaligned pointer, bad size, bad p ... */
   ATTN_ERR_UNSUPPORTED = 2,  /* valid request with no kernel (e.g. d = 96)  */
   ATTN_ERR_WORKSPACE = 3,    /* backward workspace missing or too small     */
-  ATTN_ERR_LAUNCH = 4        /* the HIP runtime rejected a kernel launch    */
+  ATTN_ERR_LAUNCH = 4,       /* the HIP runtime rejected a kernel launch    */
+  ATTN_ERR_TOO_LARGE = 5     /* beyond attn_bwd_noalloc's fixed scratch     */
 } attn_status;
 
 typedef struct {
@@ -186,6 +187,30 @@ const char* attn_status_string(attn_status s);
  * returns 0. attn_bwd and attn_bwd_stage do nothing when B or H is 0 or when
  * N = Nk = 0; with N = 0 and Nk > 0 they write dK = dV = 0, and with Nk = 0
  * and N > 0 they write dQ = 0 (each row sees no key: O = 0, lse = -inf). */
+
+/* The backward of attn_bwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). It takes the same arguments as
+ * attn_bwd minus the workspace and gives bit-identical results: the
+ * workspace lives in a fixed, file-scope device array of
+ * attn_bwd_noalloc_max_workspace_bytes() bytes (16 MiB) per GPU, held by each
+ * GPU the library runs on until the process ends. Nothing is allocated.
+ * Limit: attn_bwd_workspace_bytes(p) must not exceed that size (about 2^21
+ * query rows B*H*N in all); larger problems return ATTN_ERR_TOO_LARGE before
+ * anything is enqueued. Parameter errors are reported as attn_bwd reports
+ * them. The array belongs to the GPU of `stream` (the current device for the
+ * NULL stream); its address is looked up once per GPU. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (from two
+ * host threads, or on two streams with no ordering between them) race on it.
+ * Calls ordered on one stream are safe, and nothing in the array needs to
+ * start at zero. */
+attn_status attn_bwd_noalloc(const attn_params* p, const void* q, const void* k,
+                             const void* v, const void* o, const float* lse,
+                             const void* d_o, void* dq, void* dk, void* dv, void* stream);
+
+/* Size in bytes of attn_bwd_noalloc's per-GPU scratch array (its limit on
+ * attn_bwd_workspace_bytes). */
+size_t attn_bwd_noalloc_max_workspace_bytes(void);
 
 /* Library version as major*10000 + minor*100 + patch (0.3.0: Nk explicit). */
 int32_t attn_version(void);

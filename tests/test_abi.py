@@ -280,3 +280,27 @@ def test_window_sides_beyond_int32_are_clamped():
     p = attn.make_params(1, 1, 8, 64, dtype=attn.ATTN_F16, out_dtype=attn.ATTN_F16,
                          scale=0.125, window=(3, -1))
     assert (p.window_left, p.window_right, p.Nk) == (3, -1, 8)
+
+
+def test_noalloc_rejects_before_touching_a_device(lib):
+    """attn_bwd_noalloc validates like attn_bwd and checks its scratch limit
+    before any HIP call: invalid parameters, NULL pointers and problems whose
+    workspace exceeds the fixed scratch all fail on a machine with no GPU."""
+    cap = lib.attn_bwd_noalloc_max_workspace_bytes()
+    assert cap == 16 << 20
+    ptrs = _ptrs(9)
+    assert lib.attn_bwd_noalloc(ctypes.byref(_params(scale=0.0)), *ptrs, None) == 1
+    assert lib.attn_bwd_noalloc(ctypes.byref(_params(d=96)), *ptrs, None) == 2
+    bad = list(ptrs)
+    bad[3] = 0
+    assert lib.attn_bwd_noalloc(ctypes.byref(_params()), *bad, None) == 1
+    # 2^21 rows need two 8 MiB arrays plus nothing else: exactly at the limit
+    # would fit, one row-block more does not.
+    big = _params(B=1, H=64, N=1 << 15, d=64)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(big)) == cap
+    bigger = _params(B=1, H=64, N=(1 << 15) + 64, d=64)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(bigger)) > cap
+    assert lib.attn_bwd_noalloc(ctypes.byref(bigger), *ptrs, None) == 5
+    assert "scratch" in attn.status_string(5)
+    # Empty problems need no scratch and enqueue nothing.
+    assert lib.attn_bwd_noalloc(ctypes.byref(_params(B=0)), *([None] * 9), None) == 0
