@@ -73,6 +73,39 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs 
   }
 }
 
+// Dropout draws in the dK/dV kernel. A lane there holds one key j and 16 query
+// rows; the draws of keys 4t..4t+3 for one row come from one Philox4x32-10
+// call, and the four lanes of a quad hold those four keys. Each lane makes the
+// calls for 4 of the 16 rows and a 4 x 4 transpose across the quad hands every
+// lane its own word of all of them: one call per (row, 4-key group), as in the
+// forward, instead of one per element.
+//
+// Lane u of each quad holds x[w] = M[u][w]; returns y with y[g] = M[g][u]. Two
+// butterfly stages: exchange with lane u^1 (DPP quad_perm 1,0,3,2), then with
+// lane u^2 (quad_perm 2,3,0,1). b and c are bits 0 and 1 of u.
+__device__ __forceinline__ u32x4 quad_transpose4(u32x4 x, bool b, bool c) {
+  const uint32_t s0 = b ? x[0] : x[1];
+  const uint32_t s1 = b ? x[2] : x[3];
+  const uint32_t k0 = b ? x[1] : x[0];
+  const uint32_t k1 = b ? x[3] : x[2];
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0xB1, 0xF, 0xF, true);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, true);
+  // After stage 1 lane u holds M[g][w] for g in {u, u^1} and w in {b, b + 2}:
+  // y<g&1><w>>1> = (g&1 == b) ? kept : received. Stage 2 keeps w>>1 == c.
+  const uint32_t y00 = b ? r0 : k0, y01 = b ? r1 : k1;
+  const uint32_t y10 = b ? k0 : r0, y11 = b ? k1 : r1;
+  const uint32_t send0 = c ? y00 : y01, send1 = c ? y10 : y11;
+  const uint32_t keep0 = c ? y01 : y00, keep1 = c ? y11 : y10;
+  const uint32_t recv0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)send0, 0x4E, 0xF, 0xF, true);
+  const uint32_t recv1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)send1, 0x4E, 0xF, 0xF, true);
+  u32x4 y;
+  y[0] = c ? recv0 : keep0;
+  y[1] = c ? recv1 : keep1;
+  y[2] = c ? keep0 : recv0;
+  y[3] = c ? keep1 : recv1;
+  return y;
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV. Workgroup: 8 waves x 32 keys = 256 keys of one (b, h), two waves per
 // SIMD. The workgroup's K and V rows stay in LDS for the whole pass; Q and dO
@@ -264,9 +297,19 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
       auto grad = [&](u32x4 (&pa)[2], u32x4 (&sa)[2], auto masked) {
         f32x16 pz, ds;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
+        for (int e = 0; e < 4; ++e) {
+          // This lane's dropout words for rows qbase + 8 g4 + 4 hh + e,
+          // g4 = 0..3: the lane at quad position u draws row g4 = u, the
+          // transpose distributes the words.
+          u32x4 zw = u32x4{0, 0, 0, 0};
+          if (DROPOUT) {
+            const u32x4 mine = dropout_draws(
+                (uint32_t)j >> 2, (uint32_t)(qbase + 8 * (lane & 3) + 4 * hh + e), (uint32_t)h,
+                (uint32_t)b, a.seed_lo, a.seed_hi);
+            zw = quad_transpose4(mine, (lane & 1) != 0, (lane & 2) != 0);
+          }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int g4 = 0; g4 < 4; ++g4) {
             const int r = 4 * g4 + e;
             const int qi = qbase + 8 * g4 + 4 * hh + e;
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -ls4[g4][e]));
@@ -275,15 +318,11 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
                                 (j >= kv_end) | (qi >= N);
               p = dead ? 0.f : p;
             }
-            float z = 1.f;
-            if (DROPOUT) {
-              const u32x4 u = dropout_draws((uint32_t)j >> 2, (uint32_t)qi, (uint32_t)h,
-                                            (uint32_t)b, a.seed_lo, a.seed_hi);
-              z = (u[j & 3] >= a.drop_threshold) ? a.drop_rescale : 0.f;
-            }
+            const float z = DROPOUT ? ((zw[g4] >= a.drop_threshold) ? a.drop_rescale : 0.f) : 1.f;
             pz[r] = p * z;
             ds[r] = p * (dp[r] * z - dl4[g4][e]);
           }
+        }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
