@@ -18,7 +18,7 @@ from typing import Optional, Tuple
 
 import torch
 
-DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}
 
 # Fixed 64-bit dropout seed used by the padded+dropout workload.
 DROPOUT_SEED = 0x243F6A8885A308D3
@@ -98,6 +98,15 @@ VARIANTS = {
     "chunk_b4h16n2048nk16384d128_bf16_causal_bwd": Workload(
         "chunk_b4h16n2048nk16384d128_bf16_causal_bwd", B=4, H=16, N=2048, d=128,
         dtype="bf16", causal=True, n_k=16384, backward=True, seed=1007),
+    # fp8 (e4m3) forward at the sizes of the long layer (wide score range) and
+    # of the 16K-context layer: Q, K, V drawn as for those layers in float32
+    # and rounded to nearest-even e4m3.
+    "fp8_b4h16n4096d128_causal": Workload(
+        "fp8_b4h16n4096d128_causal", B=4, H=16, N=4096, d=128, dtype="e4m3",
+        causal=True, qk_std=3.0, seed=1009),
+    "fp8_b1h32n16384d128_causal": Workload(
+        "fp8_b1h32n16384d128_causal", B=1, H=32, N=16384, d=128, dtype="e4m3",
+        causal=True, seed=1010),
     # Head dimension 256: the same tokens and FLOP per layer as the 16K-context
     # layer with half the heads.
     "d256_b1h16n16384_bf16_causal_bwd": Workload(

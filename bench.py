@@ -45,6 +45,7 @@ if ROOT not in sys.path:
 
 METRIC = "fused attention TFLOP/s + % of fp16/bf16 MFMA peak, fwd and fwd+bwd"
 PEAK_BF16_TFLOPS = 2516.6          # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 5000.0           # MI355X dense fp8 (e4m3) MFMA peak
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "ctx16k_b1h32n16384d128_bf16_causal_bwd"
 FWD_WORKLOAD = "long_b4h16n4096d128_bf16_causal"
@@ -236,7 +237,8 @@ def variant_timings(attn, W, dev, reps: int = 30) -> dict:
         inp = W.make_inputs(w)
         q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
         do = inp.do.to(dev) if w.backward else None
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "e4m3" else q.dtype,
+                        device=dev)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         kw = dict(causal=w.causal, window=w.window, scale=w.scale)
         grads = ws = None
@@ -274,13 +276,15 @@ def variant_timings(attn, W, dev, reps: int = 30) -> dict:
         f_fwd = 4.0 * w.d * pairs
         fwd_tf = f_fwd / (fm * 1e-3) / 1e12
         step_tf = 3.5 * f_fwd / ((fm + bm) * 1e-3) / 1e12 if w.backward else None
+        peak = PEAK_FP8_TFLOPS if w.dtype == "e4m3" else PEAK_BF16_TFLOPS
         out[name] = {
             "B": w.B, "H": w.H, "N": w.N, "Nk": w.Nk, "d": w.d, "causal": w.causal,
-            "window": list(w.window) if w.window else None,
+            "dtype": w.dtype, "window": list(w.window) if w.window else None,
             "visible_pairs_per_head": int(pairs / (w.B * w.H)),
             "fwd_ms": round(fm, 4),
             "fwd_tflops": round(fwd_tf, 1),
-            "fwd_pct_of_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+            "peak_tflops": peak,
+            "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
         }
         if w.backward:
             out[name].update({
@@ -328,6 +332,8 @@ def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) 
 
     out = {}
     for name, w in dict(W.WORKLOADS, **W.VARIANTS).items():
+        if w.dtype == "e4m3":
+            continue    # no fp8 path among torch's standard attention ops
         inp = W.make_inputs(w)
         q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
         kv = None if inp.kv_len is None else inp.kv_len.to(dev)

@@ -15,7 +15,8 @@ the module raises if the library is missing or a call fails.
 
 q and dO are (B, H, N, d); k and v are (B, H, Nk, d) (Nk = N for
 self-attention; Nk = 0 is allowed: every row then sees no key), contiguous,
-float16 or bfloat16, d in {64, 128, 256}. Every tensor argument, including
+float16 or bfloat16, d in {64, 128, 256}; the forward also takes
+float8_e4m3fn q, k, v at d = 128 (O in bfloat16 by default, or float32). Every tensor argument, including
 caller-supplied outputs and the workspace, must be on q's device. Query i lines
 up with key i + Nk - N. window = (left, right) keeps keys at most `left` before
 and `right` after that key (-1: unbounded side; sides above 2^31 - 1, wider
@@ -31,7 +32,7 @@ from typing import Optional, Tuple
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
-ATTN_F16, ATTN_BF16, ATTN_F32 = 0, 1, 2
+ATTN_F16, ATTN_BF16, ATTN_F32, ATTN_E4M3 = 0, 1, 2, 3
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
                 3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_LAUNCH", 5: "ATTN_ERR_TOO_LARGE"}
 
@@ -142,6 +143,8 @@ def _code(dt) -> int:
         return ATTN_BF16
     if dt == torch.float32:
         return ATTN_F32
+    if dt == torch.float8_e4m3fn:
+        return ATTN_E4M3
     raise TypeError(f"unsupported dtype {dt}")
 
 
@@ -170,7 +173,9 @@ def _params_from(q, k, *, causal, kv_len, dropout_p, seed, scale, out_dtype, win
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    odt = q.dtype if out_dtype is None else out_dtype
+    # e4m3 inputs write O in bfloat16 unless float32 is asked for.
+    default_out = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    odt = default_out if out_dtype is None else out_dtype
     kv_ptr = 0
     if kv_len is not None:
         if kv_len.dtype != torch.int32 or kv_len.device != q.device or kv_len.numel() != B \

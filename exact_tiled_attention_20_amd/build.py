@@ -19,8 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_dropout_mask.hip",
-           "attn_noalloc.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip",
+           "attn_dropout_mask.hip", "attn_noalloc.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled: only scalar/vector fp32 ops are emitted.

@@ -20,11 +20,12 @@ namespace {
 
 // 0.3.0: Nk is always explicit (no "0 means N" sentinel); zero key rows and
 // zero query rows are valid problems; pointers of empty tensors may be NULL.
-constexpr int32_t kVersion = 300;
+// 0.4.0: fp8 (e4m3) forward.
+constexpr int32_t kVersion = 400;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-size_t elem_bytes(int32_t dt) { return dt == ATTN_F32 ? 4 : 2; }
+size_t elem_bytes(int32_t dt) { return dt == ATTN_F32 ? 4 : (dt == ATTN_E4M3 ? 1 : 2); }
 
 struct Range {
   uintptr_t lo, hi;
@@ -53,9 +54,11 @@ attn_status check_params(const attn_params* p) {
   if (p == nullptr) return ATTN_ERR_INVALID_ARG;
   if (p->B < 0 || p->H < 0 || p->N < 0 || p->d < 1) return ATTN_ERR_INVALID_ARG;
   if (p->Nk < 0 || p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
-  if (p->dtype != ATTN_F16 && p->dtype != ATTN_BF16 && p->dtype != ATTN_F32)
+  if (p->dtype != ATTN_F16 && p->dtype != ATTN_BF16 && p->dtype != ATTN_F32 &&
+      p->dtype != ATTN_E4M3)
     return ATTN_ERR_INVALID_ARG;
-  if (p->out_dtype != ATTN_F16 && p->out_dtype != ATTN_BF16 && p->out_dtype != ATTN_F32)
+  if (p->out_dtype != ATTN_F16 && p->out_dtype != ATTN_BF16 && p->out_dtype != ATTN_F32 &&
+      p->out_dtype != ATTN_E4M3)
     return ATTN_ERR_INVALID_ARG;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(p->scale) || !(p->scale > 0.0f)) return ATTN_ERR_INVALID_ARG;
@@ -72,11 +75,21 @@ attn_status check_params(const attn_params* p) {
   if (blocks + 8 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
   const long long key_blocks = heads * ((key_rows(p) + 255) / 256);
   if (key_blocks + 8 >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
-  // Supported kernels.
-  if (p->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  // Supported kernels (the e4m3 forward is checked by fp8_supported).
+  if (p->dtype == ATTN_F32 || p->out_dtype == ATTN_E4M3) return ATTN_ERR_UNSUPPORTED;
+  if (p->dtype == ATTN_E4M3) {
+    if (p->out_dtype != ATTN_BF16 && p->out_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (p->d != 128) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+  }
   if (p->out_dtype != p->dtype && p->out_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (p->d != 64 && p->d != 128 && p->d != 256) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
+}
+
+// The backward has no e4m3 kernels (checked after check_params).
+attn_status bwd_supported(const attn_params* p) {
+  return p->dtype == ATTN_E4M3 ? ATTN_ERR_UNSUPPORTED : ATTN_OK;
 }
 
 // A problem with no query rows, heads or batch entries: nothing to compute and
@@ -185,14 +198,17 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   a.drop_rescale = 1.0f / (1.0f - p->dropout_p);
   a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFull);
   a.seed_hi = (uint32_t)(p->seed >> 32);
-  const hipError_t e = attn::launch_fwd(p->dtype == ATTN_BF16 ? 1 : 0, p->d, mask,
-                                        dropout, p->out_dtype == ATTN_F32, a,
-                                        static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      p->dtype == ATTN_E4M3
+          ? attn::launch_fwd_fp8(mask, dropout, p->out_dtype == ATTN_F32, a,
+                                 static_cast<hipStream_t>(stream))
+          : attn::launch_fwd(p->dtype == ATTN_BF16 ? 1 : 0, p->d, mask, dropout,
+                             p->out_dtype == ATTN_F32, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 size_t attn_bwd_workspace_bytes(const attn_params* p) {
-  if (check_params(p) != ATTN_OK) return 0;
+  if (check_params(p) != ATTN_OK || bwd_supported(p) != ATTN_OK) return 0;
   // Two fp32 (B, H, N) arrays, each rounded up to 256 bytes: D_i = dO_i . O_i
   // and lse_i * log2(e).
   return 2 * ((stat_bytes(p) + 255) & ~size_t(255));
@@ -206,6 +222,8 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
                             size_t workspace_bytes, void* stream, bool validate_only = false) {
   if (stage < -1 || stage > 2) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  st = bwd_supported(p);
   if (st != ATTN_OK) return st;
   // Nothing to write: no heads, or neither query nor key rows. With query rows
   // but no keys, dQ is zero; with keys but no query rows, dK and dV are zero:

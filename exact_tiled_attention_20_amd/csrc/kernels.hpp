@@ -94,5 +94,8 @@ hipError_t launch_fwd(int dtype, int d, int mask, bool dropout, bool out_f32,
 hipError_t launch_bwd(int dtype, int d, int mask, bool dropout, bool out_f32, int stage,
                       const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dropout_mask(const MaskArgs& a, hipStream_t stream);
+// Forward on e4m3 Q, K, V (d = 128; O in bf16 or float).
+hipError_t launch_fwd_fp8(int mask, bool dropout, bool out_f32, const FwdArgs& a,
+                          hipStream_t stream);
 
 }  // namespace attn

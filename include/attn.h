@@ -81,7 +81,10 @@ extern "C" {
 typedef enum {
   ATTN_F16 = 0,   /* IEEE binary16 */
   ATTN_BF16 = 1,  /* bfloat16 */
-  ATTN_F32 = 2    /* IEEE binary32 (outputs only) */
+  ATTN_F32 = 2,   /* IEEE binary32 (outputs only) */
+  ATTN_E4M3 = 3   /* OCP FP8 E4M3 ("e4m3fn": bias 7, no infinities, max 448),
+                     one byte per element; inputs of attn_fwd only, d = 128,
+                     out_dtype BF16 or F32 (see attn_fwd) */
 } attn_dtype;
 
 typedef enum {
@@ -100,8 +103,10 @@ typedef struct {
                               N*d and Nk*d must be below 2^31 (per-head
                               index math) and the element counts of every
                               tensor below about 2^62.                     */
-  int32_t dtype;           /* attn_dtype of Q, K, V, dO: ATTN_F16 or BF16  */
-  int32_t out_dtype;       /* attn_dtype of O, dQ, dK, dV: == dtype or F32 */
+  int32_t dtype;           /* attn_dtype of Q, K, V, dO: ATTN_F16 or BF16
+                              (ATTN_E4M3 for the forward, see attn_fwd)    */
+  int32_t out_dtype;       /* attn_dtype of O, dQ, dK, dV: == dtype or F32
+                              (BF16 or F32 when dtype is ATTN_E4M3)        */
   float scale;             /* multiplies Q K^T; finite and > 0             */
   int32_t causal;          /* 0 or 1                                       */
   const int32_t* kv_len;   /* device int32[B] of valid key counts, or NULL */
@@ -121,7 +126,16 @@ typedef struct {
  * inside SRAM": per-block running max and denominator, rescaled O, final
  * O / l; the single log-sum-exp replaces the page's separate l and m.
  * SOTA-114, "The general form of the practice above it": scale, mask,
- * softmax and dropout fused between the two products.) */
+ * softmax and dropout fused between the two products.)
+ *
+ * fp8: with dtype ATTN_E4M3 (d = 128, out_dtype BF16 or F32) both products
+ * run on fp8 operands with fp32 accumulation. The scores are exact (products
+ * of e4m3 values are exact in fp32); the probabilities are rounded to e4m3
+ * relative to the running reference maximum before the product with V, and O
+ * is normalised by the fp32 sum of the unrounded probabilities, so each term
+ * of O carries a relative error of at most 2^-4 (absolute 2^-10 / L_i below
+ * 2^-6). ("Why FlashAttention Is a Kernel Story", section "When it falls
+ * down": FP8 score tiles need care with precision.) */
 attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
                      const void* v, void* o, float* lse, void* stream);
 
@@ -212,7 +226,7 @@ attn_status attn_bwd_noalloc(const attn_params* p, const void* q, const void* k,
  * attn_bwd_workspace_bytes). */
 size_t attn_bwd_noalloc_max_workspace_bytes(void);
 
-/* Library version as major*10000 + minor*100 + patch (0.3.0: Nk explicit). */
+/* Library version as major*10000 + minor*100 + patch (0.3.0: Nk explicit; 0.4.0: fp8 forward). */
 int32_t attn_version(void);
 
 #ifdef __cplusplus

@@ -114,19 +114,25 @@ def row_stats(q, k, *, scale, causal=False, kv_len=None, window=None, b=0, h=0,
     return P, L, valid
 
 
-def p_rounding_bound(P, L, v) -> np.ndarray:
+def p_rounding_bound(P, L, v, Z=None) -> np.ndarray:
     """Per-element bound on |O_fp8 - O| from rounding P to e4m3 (reading 2
-    above): sum_j max(2^-4 P_ij, 2^-10 / L_i) |V_jc|, over valid keys only
-    (P_ij = 0 elsewhere, and an invalid key contributes nothing)."""
+    above): sum_j max(2^-4 P_ij, 2^-10 / L_i) Z_ij |V_jc|, over valid keys only
+    (P_ij = 0 elsewhere, and an invalid key contributes nothing). Z is the
+    dropout factor keep / (1 - p) (rows x keys; 1 when None): a dropped term is
+    an exact zero, a kept one is rounded and then scaled."""
     v = np.abs(_f64(v))
     w = np.maximum(2.0 ** -4 * P, np.where(P > 0, 2.0 ** -10 / L[:, None], 0.0))
+    if Z is not None:
+        w = w * Z
     return w @ v
 
 
-def p_rounding_variance(P, L, v) -> np.ndarray:
+def p_rounding_variance(P, L, v, Z=None) -> np.ndarray:
     """Upper model of the variance of each element's error from rounding P:
-    sum_j max(2^-8 P_ij^2, 2^-20 / L_i^2) / 3 * V_jc^2 (independent errors,
-    each uniform within +-half an ulp)."""
+    sum_j max(2^-8 P_ij^2, 2^-20 / L_i^2) / 3 * Z_ij^2 V_jc^2 (independent
+    errors, each uniform within +-half an ulp)."""
     v = _f64(v)
     var = np.maximum(2.0 ** -8 * P * P, np.where(P > 0, 2.0 ** -20 / (L[:, None] ** 2), 0.0))
+    if Z is not None:
+        var = var * Z * Z
     return (var / 3.0) @ (v * v)

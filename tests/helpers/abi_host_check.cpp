@@ -35,6 +35,13 @@ hipError_t launch_dropout_mask(const MaskArgs&, hipStream_t) {
   ++g_mask_calls;
   return hipSuccess;
 }
+static int g_fp8_calls = 0;
+hipError_t launch_fwd_fp8(int mask, bool, bool, const FwdArgs& a, hipStream_t) {
+  ++g_fp8_calls;
+  g_fwd = a;
+  g_mask_mode = mask;
+  return hipSuccess;
+}
 }  // namespace attn
 
 static int g_failures = 0;
@@ -81,7 +88,7 @@ static attn_status bwd(const attn_params& p, size_t ws = (size_t)1 << 30, int st
 int main() {
   using namespace attn;
   // Version and status strings.
-  CHECK(attn_version() == 300);
+  CHECK(attn_version() == 400);
   for (int s = 0; s <= 5; ++s) CHECK(attn_status_string((attn_status)s) != nullptr);
 
   // Invalid fields: nothing is launched.
@@ -165,6 +172,35 @@ int main() {
     p.window_right = 0x7FFFFFFF;
     CHECK(fwd(p) == ATTN_OK && g_mask_mode == kMaskBand);
     CHECK(g_fwd.band_lo == -kBandInf && g_fwd.band_hi == kBandInf);
+  }
+  // fp8 (e4m3) forward: d = 128 with bf16 or float O only, no backward.
+  {
+    attn_params p = base();
+    p.dtype = ATTN_E4M3;
+    p.out_dtype = ATTN_BF16;
+    p.d = 128;
+    p.causal = 1;
+    const int before = g_fwd_calls;
+    CHECK(fwd(p) == ATTN_OK && g_fp8_calls == 1 && g_fwd_calls == before);
+    CHECK(g_mask_mode == kMaskCausal && g_fwd.N == 100);
+    p.out_dtype = ATTN_F32;
+    CHECK(fwd(p) == ATTN_OK && g_fp8_calls == 2);
+    p.out_dtype = ATTN_F16;
+    CHECK(fwd(p) == ATTN_ERR_UNSUPPORTED);
+    p.out_dtype = ATTN_E4M3;
+    CHECK(fwd(p) == ATTN_ERR_UNSUPPORTED);
+    p.out_dtype = ATTN_BF16;
+    p.d = 64;
+    CHECK(fwd(p) == ATTN_ERR_UNSUPPORTED);
+    p.d = 128;
+    CHECK(bwd(p) == ATTN_ERR_UNSUPPORTED && attn_bwd_workspace_bytes(&p) == 0);
+    // One byte per element: O (bf16, 2 x 3 x 100 x 128 x 2 bytes) placed just
+    // past Q's 76800 bytes does not alias it, one byte earlier it does.
+    CHECK(attn_fwd(&p, fake(0), fake(1), fake(2), (char*)fake(0) + 76800, (float*)fake(4),
+                   nullptr) == ATTN_OK);
+    CHECK(attn_fwd(&p, fake(0), fake(1), fake(2), (char*)fake(0) + 76784, (float*)fake(4),
+                   nullptr) == ATTN_ERR_INVALID_ARG);
+    CHECK(g_fp8_calls == 3);
   }
   // Empty problems and empty tensors.
   {

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_version() == 300
+    assert lib.attn_version() == 400
     for code, name in attn.STATUS_NAMES.items():
         assert attn.status_string(code).startswith(name)
     assert "unknown" in attn.status_string(99)
@@ -304,3 +304,18 @@ def test_noalloc_rejects_before_touching_a_device(lib):
     assert "scratch" in attn.status_string(5)
     # Empty problems need no scratch and enqueue nothing.
     assert lib.attn_bwd_noalloc(ctypes.byref(_params(B=0)), *([None] * 9), None) == 0
+
+
+def test_fp8_forward_validation(lib):
+    """e4m3 inputs: d = 128 with bf16 or float O is accepted (checked up to the
+    aliasing test, which fails on purpose here); other head dimensions and
+    output dtypes, and the backward, are unsupported."""
+    base = dict(dtype=attn.ATTN_E4M3, out_dtype=attn.ATTN_BF16, d=128)
+    q, k, v, o, lse = _ptrs(5)
+    assert _fwd(lib, _params(**base), [q, k, v, q, lse]) == 1           # o aliases q
+    assert _fwd(lib, _params(**dict(base, d=64))) == 2
+    assert _fwd(lib, _params(**dict(base, out_dtype=attn.ATTN_F16))) == 2
+    assert _fwd(lib, _params(**dict(base, out_dtype=attn.ATTN_E4M3))) == 2
+    assert _bwd(lib, _params(**base)) == 2
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(_params(**base))) == 0
+    assert _fwd(lib, _params(dtype=attn.ATTN_F16, out_dtype=attn.ATTN_E4M3)) == 2

@@ -157,3 +157,23 @@ def test_row_stats_match_the_definition():
         assert np.allclose(P[i, vis], e / e.sum(), rtol=0, atol=1e-15)
         assert np.all(P[i, ~vis] == 0)
         assert np.isclose(L[i], e.sum(), rtol=1e-15)
+
+
+def test_bound_with_dropout_factor():
+    """Z = keep / (1 - p): dropped terms are exact zeros, kept ones are rounded
+    then scaled; the bound weighted by Z holds on the emulation."""
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        n = 500
+        S = rng.normal(0, 1.0, n)
+        V = F8.round_e4m3(rng.normal(0, 1, (n, 8)))
+        keep = rng.random(n) >= 0.2
+        Z = keep / 0.8
+        p = np.exp(S - S.max())
+        L = np.array([p.sum()])
+        P = (p / p.sum())[None, :]
+        # emulation: zero the dropped keys' x before rounding, scale by 1/(1-p)
+        got = _emulate_row(S, V * Z[:, None])       # rounding x, then times Z V
+        ref = (P[0] * Z) @ V
+        bound = F8.p_rounding_bound(P, L, V, Z=Z[None, :])[0]
+        assert np.all(np.abs(got - ref) <= bound + 1e-12)
