@@ -15,7 +15,10 @@ Prints ONE JSON line. Options:
   --gpus N      only 1 is supported (the path runs on one GPU)
   --steps K     timed steps (default 10)
   --warmup W    untimed steps first (default 3)
-  --no-cpu-baseline   skip timing the CPU oracle on its bounded sample
+  --no-cpu-baseline   skip timing the CPU oracle on its bounded samples (every
+                      named workload; the headline entry is the backward
+                      workload's, with the host's CPU model, core count and
+                      BLAS library)
   --no-per-config     skip the forward timings on each named workload (the
                       `forward_per_config` field: median and minimum per
                       launch, roofline fractions, one cold launch at N=4096)
@@ -24,11 +27,12 @@ Prints ONE JSON line. Options:
                       against 16384 keys, each forward and forward +
                       backward, TFLOP/s over the visible query-key pairs; and
                       the forward at head dimension 256)
-  --unfused           also time standard attention as separate torch ops
+  --no-unfused        skip timing standard attention as separate torch ops
                       (matmul, mask, softmax, dropout, matmul; the backward
-                      by hand for the backward workload) against the fused
+                      by hand for the backward workloads) against the fused
                       kernels on every workload, with the extra device memory
-                      each allocates (the `unfused_comparison` field)
+                      each allocates and the largest |O difference| (the
+                      `unfused_comparison` field, on by default)
 """
 from __future__ import annotations
 
@@ -101,38 +105,83 @@ def _at_clock(tflops: float, mhz):
             "pct_of_clock_peak": round(100 * tflops / peak, 2)}
 
 
-def cpu_baseline(w, inputs, n_prefix: int = 16384, n_heads: int = 2) -> dict:
-    """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
-    the first n_heads heads of batch 0, over the causal prefix of the first
-    n_prefix tokens (the whole sequence by default), forward and backward.
-    Rows of a causal prefix see only keys inside it, so the forward of the
-    sample is exactly part of the full computation."""
-    import numpy as np
-    from oracle import attention as A
+def _host_info() -> dict:
+    """The host the oracle runs on: logical CPUs, CPU model, the BLAS library
+    numpy calls and the threads it uses."""
+    info = {"os_cpu_count": os.cpu_count(), "cpu_model": None, "blas": None,
+            "blas_threads": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(max(i.get("num_threads", 1) for i in blas))
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    n = min(n_prefix, w.N)
-    nh = min(n_heads, w.H)
-    sl = (slice(0, 1), slice(0, nh), slice(0, n))
-    q, k, v = inputs.q[sl], inputs.k[sl], inputs.v[sl]
-    do = inputs.do[sl] if inputs.do is not None else None
+        pass
+    return info
+
+
+# Bounded oracle samples per named workload (heads of batch 0 upward, all
+# rows unless a causal prefix is named); the rest of each workload is the same
+# computation on other heads, so its time is extrapolated by the head count.
+CPU_SAMPLES = {
+    "tiny_b1h2n256d64_fp16": dict(heads=2),
+    "decoder_b8h12n1024d64_fp16_causal": dict(heads=96),
+    "long_b4h16n4096d128_bf16_causal": dict(heads=8),
+    "bert_b16h16n512d64_fp16_pad_drop": dict(heads=256),
+    "ctx16k_b1h32n16384d128_bf16_causal_bwd": dict(heads=2),
+}
+
+
+def _oracle_sample(w, inputs, heads: int) -> dict:
+    """Time the fp64 oracle (as it stands) on the first `heads` heads of the
+    workload (row-major over (b, h)), forward, plus the backward when the
+    workload has one."""
+    from oracle import attention as A
+    nh = min(heads, w.B * w.H)
+    todo = [(i // w.H, i % w.H) for i in range(nh)]
+    kw = dict(scale=w.scale, causal=w.causal, kv_len=inputs.kv_len, dropout_p=w.dropout_p,
+              seed=inputs.seed, heads=todo)
     t0 = time.perf_counter()
-    A.forward(q, k, v, scale=w.scale, causal=w.causal)
-    passes = 1.0
-    if do is not None:
-        A.backward(q, k, v, do, scale=w.scale, causal=w.causal)
-        passes = 3.5
+    A.forward(inputs.q, inputs.k, inputs.v, **kw)
+    if inputs.do is not None:
+        A.backward(inputs.q, inputs.k, inputs.v, inputs.do, **kw)
     dt = time.perf_counter() - t0
-    flops = 4.0 * nh * n * n * w.d * (0.5 if w.causal else 1.0) * passes
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"batch 0, heads 0..{nh - 1}, first {n} tokens of the {w.name} inputs, "
-                      f"fp64 numpy {'fwd+bwd' if do is not None else 'fwd'} "
-                      f"({dt:.1f} s, {flops / 1e9:.0f} GFLOP)",
-            "seconds": round(dt, 3)}
+    flops = w.flops_fwd() * (3.5 if inputs.do is not None else 1.0) * nh / (w.B * w.H)
+    total_heads = w.B * w.H
+    return {"heads": nh, "of_heads": total_heads, "pass": "fwd+bwd" if inputs.do is not None
+            else "fwd", "seconds": round(dt, 3), "tflops": round(flops / dt / 1e12, 6),
+            "full_workload_seconds": round(dt * total_heads / nh, 1),
+            "full_workload_is_extrapolated": nh < total_heads}
+
+
+def cpu_baseline(W, cache: dict, headline: str) -> dict:
+    """The fp64 oracle timed on the host on a bounded sample of every named
+    workload (CPU_SAMPLES); the headline entry (value, unit, sample) is the
+    backward workload's, the others are listed per workload with the host's
+    description. Inputs are the same seeded tensors the GPU runs use."""
+    host = _host_info()
+    per = {}
+    for name, spec in CPU_SAMPLES.items():
+        w = W.WORKLOADS[name]
+        inputs = cache.get(name) or W.make_inputs(w)
+        per[name] = _oracle_sample(w, inputs, spec["heads"])
+        print(f"bench: cpu oracle {name}: {per[name]['seconds']} s", file=sys.stderr, flush=True)
+    h = per[headline]
+    return {"value": h["tflops"], "unit": "TFLOP/s",
+            "cores": host["blas_threads"] or host["os_cpu_count"], "kind": "oracle",
+            "sample": f"{h['heads']} of the {h['of_heads']} heads of {headline}, every row, "
+                      f"fp64 numpy {h['pass']} ({h['seconds']} s; the whole workload "
+                      f"extrapolates to {h['full_workload_seconds']} s)",
+            "seconds": h["seconds"], "host": host, "per_config": per}
 
 
 def per_config_forward(attn, W, dev, reuse=None, min_iters=50, min_ms=200.0) -> dict:
@@ -295,6 +344,38 @@ def variant_timings(attn, W, dev, reps: int = 30) -> dict:
     return out
 
 
+def unfused_attention(q, k, v, *, scale, dead=None, dropout_p=0.0, do=None):
+    """Standard (unfused) attention as separate torch ops, the chain the fused
+    kernel replaces: S = scale Q K^T materialised in the input dtype, -inf where
+    `dead` (a boolean mask broadcastable to S) is set, softmax, dropout (torch's
+    own RNG), O = P V. With dO also the backward written out by hand:
+    dV = P^T dO, dP = dO V^T, D = rowsum(dO * O), dS = P (dP - D),
+    dQ = scale dS K, dK = scale dS^T Q. Every right-hand matmul operand is made
+    contiguous first. Returns (O, (dQ, dK, dV) or None)."""
+    import torch
+    import torch.nn.functional as F
+    kt = k.transpose(-1, -2).contiguous()
+    s = torch.matmul(q, kt)
+    s.mul_(scale)
+    if dead is not None:
+        s.masked_fill_(dead, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    del s
+    pd = F.dropout(p, dropout_p) if dropout_p > 0 else p
+    o = torch.matmul(pd, v)
+    if do is None:
+        return o, None
+    vt = v.transpose(-1, -2).contiguous()
+    dv = torch.matmul(pd.transpose(-1, -2).contiguous(), do)
+    dp = torch.matmul(do, vt)
+    dd = (do.float() * o.float()).sum(-1, keepdim=True).to(q.dtype)
+    ds = p * (dp - dd)
+    del dp
+    dq = torch.matmul(ds, k).mul_(scale)
+    dk = torch.matmul(ds.transpose(-1, -2).contiguous(), q).mul_(scale)
+    return o, (dq, dk, dv)
+
+
 def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) -> dict:
     """Standard attention as separate torch ops against the fused kernels, on
     every named workload and variant: S = scale*Q K^T materialised in the input dtype,
@@ -306,7 +387,6 @@ def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) 
     Reports median times, the device memory each path needs beyond its inputs
     (outputs, workspace and temporaries), and the largest |O_unfused - O_fused|."""
     import torch
-    import torch.nn.functional as F
 
     def timed(fn, reps):
         fn()
@@ -384,25 +464,11 @@ def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) 
             return kt, v.transpose(-1, -2).contiguous()
 
         def unfused():
-            kt, vt = transposes()
-            s = torch.matmul(q, kt)
-            s.mul_(w.scale)
-            if dead is not None:
-                s.masked_fill_(dead, float("-inf"))
-            p = torch.softmax(s, dim=-1)
-            del s
-            pd = F.dropout(p, w.dropout_p) if w.dropout_p > 0 else p
-            o = torch.matmul(pd, v)
+            o, g = unfused_attention(q, k, v, scale=w.scale, dead=dead,
+                                     dropout_p=w.dropout_p, do=do)
             state["o"] = o
-            if do is not None:
-                dv = torch.matmul(pd.transpose(-1, -2).contiguous(), do)
-                dp = torch.matmul(do, vt)
-                dd = (do.float() * o.float()).sum(-1, keepdim=True).to(q.dtype)
-                ds = p * (dp - dd)
-                del dp
-                dq = torch.matmul(ds, k).mul_(w.scale)
-                dk = torch.matmul(ds.transpose(-1, -2).contiguous(), q).mul_(w.scale)
-                state["g"] = (dq, dk, dv)
+            if g is not None:
+                state["g"] = g
 
         def transposes_bwd():
             # The two N x Nk transposed copies of the backward, on tensors of
@@ -449,20 +515,65 @@ def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) 
     return out
 
 
+def only_workload(attn, W, dev, name: str, steps: int, warmup: int) -> int:
+    """--only: passes of one workload (forward, then the backward if the
+    workload has dO), timed with HIP events on the launch stream."""
+    import torch
+    w = W.WORKLOADS.get(name) or W.VARIANTS.get(name)
+    if w is None:
+        print(f"bench.py: unknown workload {name}", file=sys.stderr)
+        return 2
+    inp = W.make_inputs(w)
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    do = None if inp.do is None else inp.do.to(dev)
+    kv = None if inp.kv_len is None else inp.kv_len.to(dev)
+    kw = dict(causal=w.causal, window=w.window, scale=w.scale, kv_len=kv,
+              dropout_p=w.dropout_p, seed=inp.seed)
+    o, lse = attn.fwd(q, k, v, **kw)
+    grads = ws = None
+    if do is not None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws = torch.empty(max(1, attn.bwd_workspace_bytes(q, k=k, **kw)), dtype=torch.uint8,
+                         device=dev)
+
+    def one():
+        attn.fwd(q, k, v, out=o, lse=lse, **kw)
+        if do is not None:
+            attn.bwd(q, k, v, o, lse, do, out=grads, workspace=ws, **kw)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        one()
+    e1.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": name, "steps": steps,
+                      "ms_per_pass": round(e0.elapsed_time(e1) / max(steps, 1), 4),
+                      "pass": "fwd+bwd" if do is not None else "fwd"}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--unfused", action="store_true",
-                    help="add the unfused torch comparison on every workload")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the unfused torch comparison on every workload")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip timing the forward on each named workload")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the sliding-window and non-square variants")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only the forward headline workload (for profiling)")
+    ap.add_argument("--only", default=None, metavar="WORKLOAD",
+                    help="run only --steps passes (after --warmup) of the named workload or "
+                         "variant, forward and (if it has one) backward, and print their "
+                         "times: the entry point for hardware-counter runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (reference for "
                          "hardware byte counters)")
@@ -496,6 +607,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": src.numel() * 2, "launches": 3}))
         return 0
+
+    if args.only is not None:
+        return only_workload(attn, W, dev, args.only, args.steps, args.warmup)
 
     # -- forward headline workload (4 x 16 heads, N = 4096, d = 128, causal) --
     wf = W.WORKLOADS[FWD_WORKLOAD]
@@ -634,15 +748,18 @@ def main() -> int:
         "clock": clock,
         "csrc_digest": _csrc_digest(),
     }
+    print(f"bench: step {ms_per_step:.3f} ms ({value:.1f} TFLOP/s)", file=sys.stderr, flush=True)
     if not args.no_per_config:
         out["forward_per_config"] = per_config_forward(
             attn, W, dev, reuse={WORKLOAD: (q, k, v, None)})
     if not args.no_variants:
+        print("bench: variants", file=sys.stderr, flush=True)
         out["variants"] = variant_timings(attn, W, dev)
-    if args.unfused:
+    if not args.no_unfused:
+        print("bench: unfused comparison", file=sys.stderr, flush=True)
         out["unfused_comparison"] = unfused_comparison(attn, W, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inputs)
+        out["cpu_baseline"] = cpu_baseline(W, {WORKLOAD: inputs}, WORKLOAD)
     print(json.dumps(out))
     return 0
 

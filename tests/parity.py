@@ -83,3 +83,12 @@ def check_lse(got, ref: np.ndarray):
     if bad.any():
         raise AssertionError(f"lse: {bad.sum()} rows beyond bound; max err {err.max():.3e}")
     return float(err.max()) if err.size else 0.0
+
+
+def plain_excess(name: str, got, ref: np.ndarray, atol: float) -> int:
+    """Number of elements beyond the plain bound |err| <= atol (no storage
+    half-ulp added), printed for the record; not an assertion."""
+    g = to64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    n = int((~(np.abs(g - ref) <= atol)).sum())
+    print(f"  {name}: {n} of {g.size} elements beyond plain {atol:g}")
+    return n

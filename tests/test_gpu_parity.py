@@ -53,6 +53,10 @@ SWEEP = [(N, d, dt, mask, p)
          for mask in ("none", "causal", "pad", "causal_pad")
          for p in (0.0, 0.1)
          if p == 0.0 or mask in ("none", "causal_pad") or N in (65, 255)]
+# Half of the probabilities dropped (threshold 2^31) on shapes with ragged tails.
+SWEEP += [(N, d, dt, mask, 0.5) for (N, d, dt, mask) in
+          [(65, 64, "fp16", "causal_pad"), (255, 128, "bf16", "none"),
+           (1000, 128, "fp16", "causal"), (129, 64, "bf16", "pad")]]
 
 
 @pytest.mark.parametrize("N,d,dt,mask,p", SWEEP)
@@ -120,6 +124,24 @@ def test_fwd_key_shift_invariance_on_device():
     O_ref2, lse_ref2 = A.forward(inp.q, k2, inp.v, scale=0.125)
     check_close("O shifted", o2, O_ref2, O_ATOL, torch.float32)
     assert (o1 - o2).abs().max().item() < 5e-3
+
+
+def test_fwd_joint_key_value_permutation_on_device():
+    """Permuting the rows of K and V together (no causal mask, no padding)
+    leaves every row's set of (key, value) pairs unchanged: O and lse agree with
+    the unpermuted run within the accumulation-order tolerance and both match
+    the oracle."""
+    inp = W.random_case(2, 2, 700, 128, "bf16", seed=21, std=1.5)
+    perm = torch.randperm(700, generator=torch.Generator().manual_seed(22))
+    inp2 = W.Inputs(inp.q, inp.k[:, :, perm].contiguous(), inp.v[:, :, perm].contiguous(),
+                    None, None, 0)
+    o1, l1 = _run_fwd(inp, causal=False, p=0.0, out_dtype=torch.float32, scale=0.088)
+    o2, l2 = _run_fwd(inp2, causal=False, p=0.0, out_dtype=torch.float32, scale=0.088)
+    O_ref, lse_ref = A.forward(inp.q, inp.k, inp.v, scale=0.088)
+    check_close("O permuted", o2.cpu(), O_ref, O_ATOL, torch.float32)
+    check_lse(l2.cpu(), lse_ref)
+    assert (o1 - o2).abs().max().item() < 5e-3
+    assert ((l1 - l2).abs() <= 1e-5 * l1.abs().clamp(min=1)).all()
 
 
 BWD_SWEEP = [(N, d, dt, mask, p)

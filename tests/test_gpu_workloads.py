@@ -15,7 +15,7 @@ import attn_workloads as W
 import exact_tiled_attention_20_amd as attn
 from oracle import attention as A
 from oracle import philox
-from parity import GRAD_ATOL, O_ATOL, check_close, check_lse
+from parity import GRAD_ATOL, O_ATOL, check_close, check_lse, plain_excess, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -84,27 +84,34 @@ def test_dropout_mask_of_padded_workload(inputs_cache):
     assert abs(drop_rate - w.dropout_p) < 5 * np.sqrt(0.09 / keep.size)
 
 
-def test_long_forward_sampled(inputs_cache):
-    """4 x 16 heads, N = 4096, d = 128, causal, Q and K ~ 3 N(0,1): four heads
-    checked on every row, every head checked on 64 sampled rows."""
-    name = "long_b4h16n4096d128_bf16_causal"
-    w = W.WORKLOADS[name]
-    inp = _inputs(inputs_cache, name)
-    heads = _sampled_heads(w, 4, 7)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, w.N - 1],
-                                     np.random.default_rng(8).integers(0, w.N, 59)]))
+LONG = "long_b4h16n4096d128_bf16_causal"
+
+
+@pytest.fixture(scope="module")
+def long_gpu(inputs_cache):
+    w = W.WORKLOADS[LONG]
+    inp = _inputs(inputs_cache, LONG)
+    return w, inp, {odt: _gpu_forward(w, inp, odt) for odt in (inp.q.dtype, torch.float32)}
+
+
+@pytest.mark.parametrize("b", range(4))
+def test_long_forward_every_head(long_gpu, b):
+    """4 x 16 heads, N = 4096, d = 128, causal, Q and K ~ 3 N(0,1): every head on
+    every row, in both output modes (one batch entry per test)."""
+    w, inp, gpu = long_gpu
     kw = dict(scale=w.scale, causal=w.causal)
-    for odt in (inp.q.dtype, torch.float32):
-        _say(f"[{name}] gpu forward out={odt}")
-        o, lse = _gpu_forward(w, inp, odt)
-        O_h, l_h = A.forward(inp.q, inp.k, inp.v, heads=heads, **kw)
-        for (b, h) in heads:
-            check_close(f"O[{b},{h}]", o[b, h], O_h[b, h], O_ATOL, odt)
-            check_lse(lse[b, h], l_h[b, h])
-        O_r, l_r = A.forward(inp.q, inp.k, inp.v, rows=rows, **kw)
-        err, bias = check_close("O rows", o[:, :, rows], O_r, O_ATOL, odt)
-        check_lse(lse[:, :, rows], l_r)
-        _say(f"[{name}] out={odt}: rows max|err| {err:.3e}, mean signed err {bias:.2e}")
+    worst = {odt: (0.0, 0) for odt in gpu}
+    for h in range(w.H):
+        O_h, l_h = A.forward(*(t[b:b + 1, h:h + 1] for t in (inp.q, inp.k, inp.v)), **kw)
+        O_h, l_h = O_h[0, 0], l_h[0, 0]
+        for odt, (o, lse) in gpu.items():
+            err, _ = check_close(f"O[{b},{h}] out={odt}", o[b, h], O_h, O_ATOL, odt)
+            check_lse(lse[b, h], l_h)
+            n = int((~(np.abs(to64(o[b, h]) - O_h) <= O_ATOL)).sum())
+            worst[odt] = (max(worst[odt][0], err), worst[odt][1] + n)
+    for odt, (err, n) in worst.items():
+        _say(f"[{LONG}] batch {b} out={odt}: max|err| {err:.3e}; {n} of {w.H * w.N * w.d} "
+             f"elements beyond plain {O_ATOL:g}")
 
 
 CTX = "ctx16k_b1h32n16384d128_bf16_causal_bwd"
@@ -130,28 +137,40 @@ CTX_HEADS = [(0, 0), (0, 31), (0, 11), (0, 22)]
 
 
 @pytest.mark.parametrize("head", CTX_HEADS)
-def test_ctx16k_fwd_bwd_sampled(ctx_gpu, head):
+def test_ctx16k_fwd_bwd_full_head(ctx_gpu, head):
+    """Every one of the 16384 rows (O, lse, dQ) and of the 16384 key columns
+    (dK, dV) of the sampled head, against the oracle evaluated in row chunks
+    (each chunk forms its full rows of P and dS)."""
     w, inp, res = ctx_gpu
     b, h = head
-    rng = np.random.default_rng(100 + h)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 4095, 8192, w.N - 1],
-                                     rng.integers(0, w.N, 121)]))
-    cols = np.unique(np.concatenate([[0, 1, 127, 128, 8191, w.N - 2, w.N - 1],
-                                     rng.integers(0, w.N, 121)]))
+    rows = np.arange(w.N)
     kw = dict(scale=w.scale, causal=True)
-    _say(f"[{CTX}] head {head}: oracle forward on {rows.size} rows")
-    O_r, l_r = A.forward(inp.q, inp.k, inp.v, rows=rows, heads=[head], **kw)
-    _say(f"[{CTX}] head {head}: oracle backward on {rows.size} rows / {cols.size} columns")
-    dq_r, dk_r, dv_r = A.backward_sampled(inp.q, inp.k, inp.v, inp.do, heads=[head],
-                                          rows=rows, cols=cols, **kw)
+    # The oracle sees only this head (each head is independent by definition).
+    qh, kh, vh, doh = (t[b:b + 1, h:h + 1] for t in (inp.q, inp.k, inp.v, inp.do))
+    _say(f"[{CTX}] head {head}: oracle forward, all {w.N} rows")
+    O_r = np.empty((w.N, w.d))
+    l_r = np.empty(w.N)
+    for r0 in range(0, w.N, 1024):
+        rr = rows[r0:r0 + 1024]
+        O_c, l_c = A.forward(qh, kh, vh, rows=rr, **kw)
+        O_r[rr] = O_c[0, 0]
+        l_r[rr] = l_c[0, 0]
+    _say(f"[{CTX}] head {head}: oracle backward, all rows and key columns")
+    dq_r, dk_r, dv_r = (x[(0, 0)] for x in A.backward_sampled(
+        qh, kh, vh, doh, heads=[(0, 0)], rows=rows, cols=rows, **kw))
     for odt, (o, lse, dq, dk, dv) in res.items():
-        eo, _ = check_close("O", o[b, h, rows], O_r[b, h], O_ATOL, odt)
-        check_lse(lse[b, h, rows], l_r[b, h])
-        eq, bq = check_close("dQ", dq[b, h, rows], dq_r[head], GRAD_ATOL, odt)
-        ek, bk = check_close("dK", dk[b, h, cols], dk_r[head], GRAD_ATOL, odt)
-        ev, bv = check_close("dV", dv[b, h, cols], dv_r[head], GRAD_ATOL, odt)
+        eo, _ = check_close("O", o[b, h], O_r, O_ATOL, odt)
+        check_lse(lse[b, h], l_r)
+        eq, bq = check_close("dQ", dq[b, h], dq_r, GRAD_ATOL, odt)
+        ek, bk = check_close("dK", dk[b, h], dk_r, GRAD_ATOL, odt)
+        ev, bv = check_close("dV", dv[b, h], dv_r, GRAD_ATOL, odt)
         _say(f"[{CTX}] head {head} out={odt}: max|err| O {eo:.2e} dQ {eq:.2e} "
              f"dK {ek:.2e} dV {ev:.2e}; mean signed dQ {bq:.1e} dK {bk:.1e} dV {bv:.1e}")
+        plain_excess("O", o[b, h], O_r, O_ATOL)
+        for name, g, r in (("dQ", dq[b, h], dq_r), ("dK", dk[b, h], dk_r),
+                           ("dV", dv[b, h], dv_r)):
+            plain_excess(name, g, r, GRAD_ATOL)
+        sys.stdout.flush()
 
 
 def test_ctx16k_gradient_invariants(ctx_gpu):

@@ -257,3 +257,26 @@ def test_sampled_forms_equal_full_forms_non_square():
     assert np.abs(sq[(1, 1)] - dq[1, 1, rows]).max() < 1e-13
     assert np.abs(sk[(1, 1)] - dk[1, 1, cols]).max() < 1e-13
     assert np.abs(sv[(1, 1)] - dv[1, 1, cols]).max() < 1e-13
+
+
+def test_single_row_and_tail_forms_equal_the_full_backward():
+    """Under a causal mask, query row r alone against keys 0..r (a non-square
+    grid, bottom-right aligned) gives row r's dQ, and the last t rows against
+    all keys give the last t key columns' dK and dV: the forms the 2^20-token
+    GPU test evaluates."""
+    g = torch.Generator().manual_seed(0)
+    N, d = 300, 16
+    q, k, v, do = (torch.randn(1, 1, N, d, generator=g, dtype=torch.float64) for _ in range(4))
+    kw = dict(scale=0.25, causal=True)
+    dq, dk, dv = A.backward(q, k, v, do, **kw)
+    for r in (0, 1, 137, N - 1):
+        dq_r, _, _ = A.backward_sampled(q[:, :, r:r + 1], k[:, :, :r + 1], v[:, :, :r + 1],
+                                        do[:, :, r:r + 1], heads=[(0, 0)], rows=[0],
+                                        cols=np.zeros(0, dtype=np.int64), row_chunk=1, **kw)
+        assert np.abs(dq_r[(0, 0)] - dq[0, 0, r:r + 1]).max() < 1e-12
+    lo = N - 40
+    _, dk_r, dv_r = A.backward_sampled(q[:, :, lo:], k, v, do[:, :, lo:], heads=[(0, 0)],
+                                       rows=np.zeros(0, dtype=np.int64),
+                                       cols=np.arange(lo, N), row_chunk=8, **kw)
+    assert np.abs(dk_r[(0, 0)] - dk[0, 0, lo:]).max() < 1e-12
+    assert np.abs(dv_r[(0, 0)] - dv[0, 0, lo:]).max() < 1e-12
