@@ -192,7 +192,15 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   a.per_xcd = (a.total + 7) / 8;
   a.scale = p->scale;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
-  a.rescale_thr = 8.0f / a.scale_log2;
+  // How far (log2 of probability) a row maximum may exceed the reference
+  // before the reference is raised: probabilities up to 2^bits relative to it
+  // are formed and rounded into the operand type of the P V product, so the
+  // bound is that type's range -- e4m3 holds 448 (2^8 is used), fp16 65504
+  // (2^15), bf16 the fp32 exponent range (2^64 leaves the fp32 sums far from
+  // overflow). Rounding is relative, so the value does not change accuracy;
+  // a larger bound only makes the O rescale rarer.
+  const float bits = p->dtype == ATTN_E4M3 ? 8.0f : (p->dtype == ATTN_F16 ? 15.0f : 64.0f);
+  a.rescale_thr = bits / a.scale_log2;
   const bool dropout = p->dropout_p > 0.0f;
   a.drop_threshold = drop_threshold(p->dropout_p);
   a.drop_rescale = 1.0f / (1.0f - p->dropout_p);

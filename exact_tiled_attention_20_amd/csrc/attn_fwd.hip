@@ -137,8 +137,9 @@ void attn_fwd_kernel(const FwdArgs a) {
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   // m_ref: reference maximum (raw q.k units) that the exponentials are taken
   // against. It is raised only when a tile's row maximum exceeds it by more
-  // than 2^8 in probability, so the O rescale runs rarely; O and l always
-  // share the same reference, which keeps O / l exact.
+  // than the operand type's range allows (2^64 in probability for bf16, 2^15
+  // for fp16), so the O rescale runs rarely even when the scores spread widely;
+  // O and l always share the same reference, which keeps O / l exact.
   float m_ref = -INFINITY;
   // This half-lane's share of the running denominator, twice: l sums the fp32
   // probabilities (it defines lse); lr sums the same probabilities rounded to

@@ -48,7 +48,8 @@ struct FwdArgs {
   float scale;           // softmax scale (fp32)
   float scale_log2;      // scale * log2(e)
   float rescale_thr;     // raise the reference max when a row max exceeds it
-                         // by this much (raw q.k units): 8 / scale_log2
+                         // by this much (raw q.k units): bits / scale_log2,
+                         // bits = 64 (bf16), 15 (fp16), 8 (e4m3)
   uint32_t drop_threshold;  // keep iff draw >= threshold
   float drop_rescale;       // 1 / (1 - p)
   uint32_t seed_lo, seed_hi;

@@ -126,6 +126,29 @@ def test_fwd_key_shift_invariance_on_device():
     assert (o1 - o2).abs().max().item() < 5e-3
 
 
+@pytest.mark.parametrize("dt,step", [("fp16", 10.0), ("bf16", 40.0), ("bf16", 11.0)])
+def test_fwd_reference_raised_near_the_operand_range(dt, step):
+    """Row maxima that climb by `step` (natural-log units) from one 64-key tile
+    to the next: just under the distance at which the kernel raises its
+    reference (2^15 in probability for fp16, 2^64 for bf16), so the
+    probabilities it forms and rounds reach nearly the largest the operand
+    type holds before a raise. Against the oracle, float32 output."""
+    N, d = 512, 64
+    g = torch.Generator().manual_seed(int(step))
+    q = torch.zeros(1, 2, N, d)
+    q[..., 0] = 8.0                         # scale * q.k = k[..., 0] with scale 1/8
+    k = torch.randn(1, 2, N, d, generator=g) * 0.5
+    k[..., 0] = step * (torch.arange(N) // 64).float() + torch.rand(N, generator=g)
+    v = torch.randn(1, 2, N, d, generator=g)
+    dtype = W.DTYPES[dt]
+    inp = W.Inputs(q.to(dtype), k.to(dtype), v.to(dtype), None, None, 0)
+    for causal in (False, True):
+        o, lse = _run_fwd(inp, causal=causal, p=0.0, out_dtype=torch.float32, scale=0.125)
+        O_ref, lse_ref = A.forward(inp.q, inp.k, inp.v, scale=0.125, causal=causal)
+        check_close(f"O {dt} step {step}", o.cpu(), O_ref, O_ATOL, torch.float32)
+        check_lse(lse.cpu(), lse_ref)
+
+
 def test_fwd_joint_key_value_permutation_on_device():
     """Permuting the rows of K and V together (no causal mask, no padding)
     leaves every row's set of (key, value) pairs unchanged: O and lse agree with
