@@ -516,8 +516,10 @@ def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) 
 
 
 def only_workload(attn, W, dev, name: str, steps: int, warmup: int) -> int:
-    """--only: passes of one workload (forward, then the backward if the
-    workload has dO), timed with HIP events on the launch stream."""
+    """--only: passes of one workload (forward, then the backward wherever the
+    input dtype has one: e4m3 is forward-only), timed with HIP events on the
+    launch stream. A workload without its own dO gets one drawn from N(0, 1)
+    with its seed + 1, so that counter runs cover every backward instance."""
     import torch
     w = W.WORKLOADS.get(name) or W.VARIANTS.get(name)
     if w is None:
@@ -526,6 +528,9 @@ def only_workload(attn, W, dev, name: str, steps: int, warmup: int) -> int:
     inp = W.make_inputs(w)
     q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
     do = None if inp.do is None else inp.do.to(dev)
+    if do is None and w.dtype != "e4m3":
+        g = torch.Generator().manual_seed(w.seed + 1)
+        do = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
     kv = None if inp.kv_len is None else inp.kv_len.to(dev)
     kw = dict(causal=w.causal, window=w.window, scale=w.scale, kv_len=kv,
               dropout_p=w.dropout_p, seed=inp.seed)
@@ -572,8 +577,8 @@ def main() -> int:
                     help="time only the forward headline workload (for profiling)")
     ap.add_argument("--only", default=None, metavar="WORKLOAD",
                     help="run only --steps passes (after --warmup) of the named workload or "
-                         "variant, forward and (if it has one) backward, and print their "
-                         "times: the entry point for hardware-counter runs")
+                         "variant, forward and backward (forward only for e4m3), and print "
+                         "their times: the entry point for hardware-counter runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (reference for "
                          "hardware byte counters)")
