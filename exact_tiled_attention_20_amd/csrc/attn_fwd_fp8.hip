@@ -21,8 +21,11 @@
 //     of that step of query row l%32 (hh = l/32), the MFMA B operand.
 //   * K and V tiles of 64 keys x 128 bytes are copied HBM -> LDS directly,
 //     double-buffered, K one tile ahead of V. A row's 16-byte chunk c is stored
-//     at chunk position c ^ ((row >> 1) & 7): the K row reads (32 rows, one
-//     chunk each) and the 8-row transposed V reads both touch every bank once.
+//     at chunk position c ^ s(row), s = bits 1..3 of the row with the lower two
+//     exchanged: the K row reads (16 rows of 128 bytes per 256-byte bank sweep,
+//     one chunk each) and the transposed V reads (32 lanes of 8 bytes per sweep,
+//     8 keys, chunks 2db and 2db + 1) both touch every bank once. With s = bits
+//     1..3 unpermuted, the two 16-lane halves of a V read met in the same banks.
 //   * The MFMA pairs byte t of lane l in A with byte t of lane l in B (rows and
 //     columns l%32); any assignment of the 64 k indices to (hh, t) works if A
 //     and B share it. The S^T accumulator holds, in lane l (query l%32) and
@@ -56,8 +59,11 @@ constexpr int kF8Row = kF8D;        // bytes per K/V row
 constexpr int kF8BC = 64;           // keys per tile
 constexpr int kF8Tile = kF8BC * kF8Row;  // 8 KiB
 
-// Chunk position of 16-byte chunk c of tile row `row`.
-__device__ __forceinline__ int f8_chunk(int row, int c) { return c ^ ((row >> 1) & 7); }
+// Chunk position of 16-byte chunk c of tile row `row` (an involution in c).
+__device__ __forceinline__ int f8_chunk(int row, int c) {
+  const int j = (row >> 1) & 7;
+  return c ^ ((j & 4) | ((j & 1) << 1) | ((j >> 1) & 1));
+}
 
 // C = A B + C on e4m3 operands (format code 0 for both; no block scaling).
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
