@@ -135,9 +135,9 @@ def _host_info() -> dict:
 CPU_SAMPLES = {
     "tiny_b1h2n256d64_fp16": dict(heads=2),
     "decoder_b8h12n1024d64_fp16_causal": dict(heads=96),
-    "long_b4h16n4096d128_bf16_causal": dict(heads=8),
+    "long_b4h16n4096d128_bf16_causal": dict(heads=64),
     "bert_b16h16n512d64_fp16_pad_drop": dict(heads=256),
-    "ctx16k_b1h32n16384d128_bf16_causal_bwd": dict(heads=2),
+    "ctx16k_b1h32n16384d128_bf16_causal_bwd": dict(heads=4),
 }
 
 
