@@ -20,18 +20,21 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip",
-           "attn_dropout_mask.hip", "attn_noalloc.hip"]
+           "attn_bwd_dq256.hip", "attn_dropout_mask.hip", "attn_noalloc.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled: only scalar/vector fp32 ops are emitted.
-# MFMA results are placed in VGPRs rather than AGPRs, so the softmax arithmetic
-# that consumes score tiles needs no accumulator-register copies.
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
+# MFMA results placed in VGPRs rather than AGPRs, so the softmax arithmetic
+# that consumes score tiles needs no accumulator-register copies. Every source
+# but the d = 256 dQ kernel's, whose Q and dO operands the flag would push into
+# the accumulation registers (copied back before every MFMA).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_VGPR_FORM = {"attn_bwd_dq256.hip"}
 
 
 def hipcc() -> str:
@@ -43,7 +46,8 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    flags = COMMON_FLAGS + ([] if src in NO_VGPR_FORM else VGPR_FORM)
+    cmd = [hipcc(), *flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -19,7 +19,8 @@
 //      registers of P and dS, rounded to the input dtype, are then directly the
 //      A operands of dV = P^T dO and dK = dS^T Q, and dO and Q are fed as B
 //      operands by ds_read_b64_tr_b16 from their row-major LDS tiles.
-//   3. dQ: one workgroup per 128 queries (4 waves x 32 queries), the forward's
+//   3. dQ (attn_bwd_dq.hpp; the d = 256 instances in attn_bwd_dq256.hip): one
+//      workgroup per 128 queries (4 waves x 32 queries), the forward's
 //      orientation (S^T = K Q^T, one query per lane) plus dP^T = V dO^T; dQ^T =
 //      K^T dS^T reads K transposed from LDS. Deterministic: no atomics.
 // Banded masks (causal, sliding window, non-square alignment) arrive as the key
@@ -28,12 +29,11 @@
 // kernel only the key tiles its rows see.
 #include <type_traits>
 
+#include "attn_bwd_dq.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace attn {
-
-constexpr float kLog2e = 1.4426950408889634f;
 
 template <bool OUT_F32, typename E>
 __device__ __forceinline__ float load_out(const void* p, size_t idx) {
@@ -282,11 +282,30 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
         s[r] = 0.f;
         dp[r] = 0.f;
       }
+      if constexpr (D > 128) {
+        // One wave per SIMD: nothing else hides the LDS latency, so each
+        // k-step's four fragments are read one step ahead.
+        u32x4 fq[2], fo[2], fk[2], fv[2];
+        auto rd = [&](int kk, int i) {
+          fq[i] = *(const u32x4*)(qb + roff[kk]);
+          fo[i] = *(const u32x4*)(ob + roff[kk]);
+          fk[i] = *(const u32x4*)(smem + kvoff[kk]);
+          fv[i] = *(const u32x4*)(smem + kvoff[kk] + KV_WAVE);
+        };
+        rd(0, 0);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s = E::mfma(*(const u32x4*)(qb + roff[kk]), *(const u32x4*)(smem + kvoff[kk]), s);
-        dp = E::mfma(*(const u32x4*)(ob + roff[kk]),
-                     *(const u32x4*)(smem + kvoff[kk] + KV_WAVE), dp);
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 1 < KK) rd(kk + 1, (kk + 1) & 1);
+          s = E::mfma(fq[kk & 1], fk[kk & 1], s);
+          dp = E::mfma(fo[kk & 1], fv[kk & 1], dp);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          s = E::mfma(*(const u32x4*)(qb + roff[kk]), *(const u32x4*)(smem + kvoff[kk]), s);
+          dp = E::mfma(*(const u32x4*)(ob + roff[kk]),
+                       *(const u32x4*)(smem + kvoff[kk] + KV_WAVE), dp);
+        }
       }
 
       // P (masked), dropout, dS; packed as MFMA A operands for 16-query steps.
@@ -391,222 +410,6 @@ write_out:
     }
 }
 
-// ---------------------------------------------------------------------------
-// dQ. Workgroup: 128 queries of one (b, h); wave w owns 32 query rows. The
-// forward's orientation: S^T = K Q^T and dP^T = V dO^T put one query per lane,
-// so lse_i and D_i are per-lane scalars, and the packed dS^T registers are the
-// B operand of dQ^T += K^T dS^T (K read transposed from LDS). K/V tiles of 64
-// keys are copied HBM -> LDS directly; each tile is processed as two 32-key
-// halves to keep two waves per SIMD.
-template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
-__global__ __launch_bounds__(kBwdThreads)
-__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
-void attn_bwd_dq_kernel(const BwdArgs a) {
-  constexpr int BR = 128;
-  constexpr int BC = 64;
-  constexpr int KK = D / 16;
-  constexpr int NDB = D / 32;
-  constexpr int TILE_BYTES = BC * D * 2;
-  constexpr bool BAND = MASK != kMaskNone;
-  constexpr bool LO = MASK == kMaskBand;   // a lower band edge exists
-
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
-
-  const int nqb = (a.N + BR - 1) / BR;
-  const WorkItem wi = decode_work_item(blockIdx.x, a.B * a.H, nqb);
-  if (!wi.valid) return;
-  const int bh = wi.bh;
-  const int qblk = BAND ? nqb - 1 - wi.rank : wi.rank;  // heaviest first
-  const int b = bh / a.H;
-  const int h = bh - b * a.H;
-  const int N = a.N;
-  const int q0 = qblk * BR;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const size_t khead = (size_t)bh * (size_t)a.Nk * D;
-  const uint16_t* __restrict__ Q = a.q + head;
-  const uint16_t* __restrict__ K = a.k + khead;
-  const uint16_t* __restrict__ V = a.v + khead;
-  const uint16_t* __restrict__ dO = a.d_o + head;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  int kv_end = a.Nk;
-  if (a.kv_len != nullptr) kv_end = min(max(a.kv_len[b], 0), a.Nk);
-  const int band_lo = LO ? a.band_lo : -kBandInf;
-  const int band_hi = MASK == kMaskCausal ? 0 : a.band_hi;
-  // Key tiles [t0, ntiles) hold every key a row of this block sees.
-  int kend = kv_end;
-  int t0 = 0;
-  if (BAND) {
-    kend = min(kend, max(0, min(q0 + BR, N) + band_hi));
-    if (LO) t0 = max(0, q0 + band_lo) / BC;
-  }
-  const int ntiles = (kend + BC - 1) / BC;
-
-  const int wq0 = q0 + 32 * w;
-  const int qi = wq0 + l32;
-  const bool wave_has_rows = wq0 < N;
-
-  u32x4 qf[KK], of[KK];
-  float lse2 = INFINITY, dlt = 0.f;
-  {
-    const int qr = min(qi, N - 1);
-    const uint16_t* qs = Q + (size_t)qr * D + hh * 8;
-    const uint16_t* os = dO + (size_t)qr * D + hh * 8;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      qf[kk] = *(const u32x4*)(qs + kk * 16);
-      of[kk] = *(const u32x4*)(os + kk * 16);
-    }
-    if (qi < N) {
-      const float x = a.lse[(size_t)bh * N + qi];
-      lse2 = (x == -INFINITY) ? INFINITY : x * kLog2e;
-      dlt = a.delta[(size_t)bh * N + qi];
-    }
-  }
-
-  char* const kb0 = smem;
-  char* const vb0 = smem + 2 * TILE_BYTES;
-  TilePairLoader<D, BC, 4> loader;
-  loader.init(w, lane);
-
-  int roff[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) roff[kk] = lds_off<D>(l32, (kk * 2 + hh) * 16);
-  const int g = lane >> 4;
-  const int i16 = lane & 15;
-  int toff[2][NDB];
-#pragma unroll
-  for (int half = 0; half < 2; ++half)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      toff[half][db] = lds_off<D>(4 * hh + (i16 >> 2) + 8 * half,
-                                  (32 * db + 16 * (g & 1) + 4 * (i16 & 3)) * 2);
-
-  f32x16 acc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  const float c2 = a.scale_log2;
-
-  if (ntiles > t0) loader.issue(K, V, t0 * BC, kv_end, kb0, vb0);
-  // The loop body is instantiated once per buffer (the loop is unrolled by
-  // two), so every LDS address is a per-lane offset plus a constant that the
-  // read instructions carry as their immediate offset.
-  auto tile_step = [&](int t, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    wait_all_memory();
-    __syncthreads();
-    // Untracked, so that no LDS read of tile t waits for this prefetch; the
-    // wait at the top of the next iteration orders it before its readers.
-    if (t + 1 < ntiles) {
-      loader.issue_one_untracked(K, (t + 1) * BC, kv_end, kb0 + (buf ^ 1) * TILE_BYTES);
-      loader.issue_one_untracked(V, (t + 1) * BC, kv_end, vb0 + (buf ^ 1) * TILE_BYTES);
-    }
-    const int k0 = t * BC;
-    const bool active = wave_has_rows &&
-                        (!BAND || (k0 <= wq0 + 31 + band_hi &&
-                                   (!LO || k0 + BC - 1 >= wq0 + band_lo)));
-    if (!active) return;
-    const char* kb = kb0 + buf * TILE_BYTES;
-    const char* vb = vb0 + buf * TILE_BYTES;
-    const bool need_mask =
-        (BAND && (k0 + BC - 1 > wq0 + band_hi || (LO && k0 < wq0 + 31 + band_lo))) ||
-        (k0 + BC > kv_end);
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      // S^T and dP^T for keys k0 + 32 kb2 .. +32 (lane = query).
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-      const int rbase = kb2 * 32 * D * 2;
-      // Interleaved chains: a single dependent MFMA chain cannot issue at
-      // the full rate.
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s = E::mfma(*(const u32x4*)(kb + rbase + roff[kk]), qf[kk], s);
-        dp = E::mfma(*(const u32x4*)(vb + rbase + roff[kk]), of[kk], dp);
-      }
-      // dS^T = P^T (Z dP^T - D); register r is key k0 + 32kb2 + 8(r/4) + 4hh + r%4.
-      // The masked form is a separate instantiation, so the unmasked tiles
-      // run branch-free.
-      auto grad = [&](auto masked) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int j0 = k0 + kb2 * 32 + 8 * g4 + 4 * hh;
-          u32x4 u = u32x4{0, 0, 0, 0};
-          if (DROPOUT)
-            u = dropout_draws((uint32_t)j0 >> 2, (uint32_t)qi, (uint32_t)h, (uint32_t)b,
-                              a.seed_lo, a.seed_hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
-            if (decltype(masked)::value) {
-              const int jj = j0 + e;
-              p = ((BAND && (jj > qi + band_hi || (LO && jj < qi + band_lo))) || jj >= kv_end)
-                      ? 0.f : p;
-            }
-            float dpz = dp[r];
-            if (DROPOUT) dpz = (u[e] >= a.drop_threshold) ? dpz * a.drop_rescale : 0.f;
-            s[r] = p * (dpz - dlt);
-          }
-        }
-      };
-      if (need_mask)
-        grad(std::true_type());
-      else
-        grad(std::false_type());
-      // dQ^T += K^T dS^T, two 16-key MFMA steps.
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        u32x4 sb;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sb[e] = E::pack2(s[8 * c + 2 * e], s[8 * c + 2 * e + 1]);
-        const int tbase = (kb2 * 2 + c) * 16 * D * 2;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(kb, tbase + toff[0][db]));
-          const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(kb, tbase + toff[1][db]));
-          acc[db] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, sb, acc[db]);
-        }
-      }
-    }
-  };
-  // Buffers are counted from t0: tile t lives in buffer (t - t0) & 1.
-  for (int t = t0; t < ntiles; t += 2) {
-    tile_step(t, std::integral_constant<int, 0>());
-    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
-  }
-
-  if (qi < N) {
-    const size_t orow = head + (size_t)qi * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dcol = 32 * db + 8 * g4 + 4 * hh;
-        const float v0 = acc[db][4 * g4 + 0] * a.scale;
-        const float v1 = acc[db][4 * g4 + 1] * a.scale;
-        const float v2 = acc[db][4 * g4 + 2] * a.scale;
-        const float v3 = acc[db][4 * g4 + 3] * a.scale;
-        if (OUT_F32) {
-          *(f32x4*)((float*)a.dq + orow + dcol) = f32x4{v0, v1, v2, v3};
-        } else {
-          *(u32x2*)((uint16_t*)a.dq + orow + dcol) = u32x2{E::pack2(v0, v1), E::pack2(v2, v3)};
-        }
-      }
-  }
-}
-
 template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
   // A kernel with no work item is not launched (a zero-sized grid is a launch
@@ -631,11 +434,17 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if ((stage < 0 || stage == 2) && a.N > 0) {
-    const int nqb = (a.N + 127) / 128;
-    const int tq = a.B * a.H * nqb;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<E, D, MASK, DROPOUT, OUT_F32>),
-                       dim3(((tq + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
-    e = hipGetLastError();
+    if constexpr (D > 128) {
+      // Built in its own translation unit with other code-generation flags.
+      e = launch_bwd_dq256(std::is_same<E, Elem<bf16_t>>::value ? 1 : 0, MASK, DROPOUT, OUT_F32,
+                           a, stream);
+    } else {
+      const int nqb = (a.N + 127) / 128;
+      const int tq = a.B * a.H * nqb;
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<E, D, MASK, DROPOUT, OUT_F32>),
+                         dim3(((tq + 7) / 8) * 8), dim3(kBwdThreads), 0, stream, a);
+      e = hipGetLastError();
+    }
   }
   return e;
 }

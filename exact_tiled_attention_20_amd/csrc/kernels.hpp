@@ -94,6 +94,9 @@ hipError_t launch_fwd(int dtype, int d, int mask, bool dropout, bool out_f32,
 // stage: -1 = all three kernels, else 0 (preprocess), 1 (dK/dV), 2 (dQ).
 hipError_t launch_bwd(int dtype, int d, int mask, bool dropout, bool out_f32, int stage,
                       const BwdArgs& a, hipStream_t stream);
+// The dQ kernel at d = 256 (its own translation unit; called by launch_bwd).
+hipError_t launch_bwd_dq256(int dtype, int mask, bool dropout, bool out_f32, const BwdArgs& a,
+                            hipStream_t stream);
 hipError_t launch_dropout_mask(const MaskArgs& a, hipStream_t stream);
 // Forward on e4m3 Q, K, V (d = 128; O in bf16 or float).
 hipError_t launch_fwd_fp8(int mask, bool dropout, bool out_f32, const FwdArgs& a,
