@@ -21,9 +21,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 // B operand of dQ^T += K^T dS^T (K read transposed from LDS). K/V tiles of 64
 // keys are copied HBM -> LDS directly; each tile is processed as two 32-key
 // halves to keep two waves per SIMD.
+// Waves per SIMD the register budget is set for: one at d = 256; three at
+// d = 64 (168 registers; 32 KiB of LDS per workgroup) except the unmasked
+// dropout instance, which would spill; two otherwise.
+template <int D, int MASK, bool DROPOUT>
+constexpr int dq_waves_per_simd() {
+  return D > 128 ? 1 : (D < 128 && !(DROPOUT && MASK == kMaskNone)) ? 3 : 2;
+}
+
 template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 __global__ __launch_bounds__(kBwdThreads)
-__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
+__attribute__((amdgpu_waves_per_eu(dq_waves_per_simd<D, MASK, DROPOUT>(),
+                                   dq_waves_per_simd<D, MASK, DROPOUT>())))
 void attn_bwd_dq_kernel(const BwdArgs a) {
   constexpr int BR = 128;
   constexpr int BC = 64;

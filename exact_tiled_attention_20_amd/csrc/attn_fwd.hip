@@ -41,9 +41,19 @@
 
 namespace attn {
 
+// Waves per SIMD the register budget is set for: one at d = 256; three at
+// d = 64 without dropout or a two-sided band (those instances fit in 168
+// registers, and the small grids of d = 64 layers then stay resident in one
+// round of three 32 KiB-LDS workgroups per CU); two otherwise.
+template <int D, int MASK, bool DROPOUT>
+constexpr int fwd_waves_per_simd() {
+  return D > 128 ? 1 : (D < 128 && !DROPOUT && MASK != kMaskBand) ? 3 : 2;
+}
+
 template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 __global__ __launch_bounds__(kFwdThreads)
-__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd<D, MASK, DROPOUT>(),
+                                   fwd_waves_per_simd<D, MASK, DROPOUT>())))
 void attn_fwd_kernel(const FwdArgs a) {
   constexpr int BR = kFwdBlockQ;
   constexpr int BC = kFwdBlockK;
