@@ -11,8 +11,9 @@
 //
 // Three kernels on the caller's stream:
 //   1. preprocess: D_i for every row (HBM-bound, 16 lanes per row).
-//   2. dK/dV: one workgroup per 256 keys (8 waves x 32 keys, two waves per
-//      SIMD). K and V rows stay in LDS for the whole pass; Q and dO stream
+//   2. dK/dV: one workgroup per 256 keys at d = 128 (8 waves x 32 keys, two
+//      waves per SIMD; 128 keys and 4 waves at d = 64 and d = 256). K and V
+//      rows stay in LDS for the whole pass; Q and dO stream
 //      through LDS in tiles of 32 queries; lse and D come from L2 into
 //      registers. Scores are computed as S = Q K^T so that each lane owns one
 //      key and the query index runs along the accumulator registers: the fp32
@@ -107,16 +108,19 @@ __device__ __forceinline__ u32x4 quad_transpose4(u32x4 x, bool b, bool c) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV. Workgroup: 8 waves x 32 keys = 256 keys of one (b, h), two waves per
-// SIMD. The workgroup's K and V rows stay in LDS for the whole pass; Q and dO
-// tiles of 32 query rows stream HBM -> LDS directly, double-buffered (for
-// d = 128 that fills the 160 KiB of LDS exactly); lse and D of the tile's rows
-// are read from L2 into registers.
+// dK, dV. Workgroup at d = 128: 8 waves x 32 keys = 256 keys of one (b, h),
+// two waves per SIMD. The workgroup's K and V rows stay in LDS for the whole
+// pass; Q and dO tiles of 32 query rows stream HBM -> LDS directly,
+// double-buffered (for d = 128 that fills the 160 KiB of LDS exactly); lse and
+// D of the tile's rows are read from L2 into registers.
 constexpr int kDkdvWaves = 8;
-// d = 256: 4 waves (128 keys, 128 KiB of K/V rows) at one wave per SIMD, and a
-// single Q tile and dO tile of 16 KiB each: 160 KiB of LDS in all.
+// d = 64: 4 waves (128 keys, 48 KiB of LDS), so two workgroups share a CU and
+// the short grids of d = 64 layers (a few key blocks per head) spread over
+// twice as many workgroups. d = 256: 4 waves (128 keys, 128 KiB of K/V rows)
+// at one wave per SIMD, and a single Q tile and dO tile of 16 KiB each:
+// 160 KiB of LDS in all.
 template <int D>
-constexpr int dkdv_waves() { return D > 128 ? 4 : kDkdvWaves; }
+constexpr int dkdv_waves() { return D == 128 ? kDkdvWaves : 4; }
 
 template <typename E, int D, int MASK, bool DROPOUT, bool OUT_F32>
 __global__ __launch_bounds__(64 * dkdv_waves<D>())
