@@ -153,11 +153,13 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       // S^T and dP^T for keys k0 + 32 kb2 .. +32 (lane = query).
+      // Without dropout the dP^T chain starts from -D (one value per lane:
+      // this lane's query row), so dS^T = P^T dP'^T needs no subtraction.
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[r] = 0.f;
-        dp[r] = 0.f;
+        dp[r] = DROPOUT ? 0.f : -dlt;
       }
       const int rbase = kb2 * 32 * D * 2;
       // Interleaved chains: a single dependent MFMA chain cannot issue at
@@ -204,9 +206,12 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
               p = ((BAND && (jj > qi + band_hi || (LO && jj < qi + band_lo))) || jj >= kv_end)
                       ? 0.f : p;
             }
-            float dpz = dp[r];
-            if (DROPOUT) dpz = (u[e] >= a.drop_threshold) ? dpz * a.drop_rescale : 0.f;
-            s[r] = p * (dpz - dlt);
+            if (DROPOUT) {
+              const float dpz = (u[e] >= a.drop_threshold) ? dp[r] * a.drop_rescale : 0.f;
+              s[r] = p * (dpz - dlt);
+            } else {
+              s[r] = p * dp[r];
+            }
           }
         }
       };
