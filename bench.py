@@ -33,6 +33,13 @@ Prints ONE JSON line. Options:
                       kernels on every workload, with the extra device memory
                       each allocates and the largest |O difference| (the
                       `unfused_comparison` field, on by default)
+  --only WORKLOAD     only --steps passes of one workload (forward and
+                      backward), for hardware-counter runs
+  --inputs KIND       with --only: `drawn` (the workload's own inputs, the
+                      default), `zeros` (Q, K, V and dO all zero) or `signs`
+                      (each drawn value replaced by its sign). The kernels
+                      execute the same instructions on all three; the chip's
+                      clock does not stay the same.
 """
 from __future__ import annotations
 
@@ -515,7 +522,7 @@ def unfused_comparison(attn, W, dev, reps_small: int = 20, reps_large: int = 5) 
     return out
 
 
-def only_workload(attn, W, dev, name: str, steps: int, warmup: int) -> int:
+def only_workload(attn, W, dev, name: str, steps: int, warmup: int, inputs: str = "drawn") -> int:
     """--only: passes of one workload (forward, then the backward wherever the
     input dtype has one: e4m3 is forward-only), timed with HIP events on the
     launch stream. A workload without its own dO gets one drawn from N(0, 1)
@@ -531,6 +538,14 @@ def only_workload(attn, W, dev, name: str, steps: int, warmup: int) -> int:
     if do is None and w.dtype != "e4m3":
         g = torch.Generator().manual_seed(w.seed + 1)
         do = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+    if inputs != "drawn":
+        # Same shapes and dtypes, other bit patterns: all zero, or +-1.
+        def recast(x):
+            if x is None:
+                return None
+            y = torch.zeros_like(x.float()) if inputs == "zeros" else torch.sign(x.float())
+            return y.to(x.dtype)
+        q, k, v, do = recast(q), recast(k), recast(v), recast(do)
     kv = None if inp.kv_len is None else inp.kv_len.to(dev)
     kw = dict(causal=w.causal, window=w.window, scale=w.scale, kv_len=kv,
               dropout_p=w.dropout_p, seed=inp.seed)
@@ -555,7 +570,7 @@ def only_workload(attn, W, dev, name: str, steps: int, warmup: int) -> int:
         one()
     e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"workload": name, "steps": steps,
+    print(json.dumps({"workload": name, "inputs": inputs, "steps": steps,
                       "ms_per_pass": round(e0.elapsed_time(e1) / max(steps, 1), 4),
                       "pass": "fwd+bwd" if do is not None else "fwd"}))
     return 0
@@ -579,6 +594,8 @@ def main() -> int:
                     help="run only --steps passes (after --warmup) of the named workload or "
                          "variant, forward and backward (forward only for e4m3), and print "
                          "their times: the entry point for hardware-counter runs")
+    ap.add_argument("--inputs", default="drawn", choices=("drawn", "zeros", "signs"),
+                    help="with --only: the workload's drawn inputs, all zeros, or their signs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (reference for "
                          "hardware byte counters)")
@@ -614,7 +631,7 @@ def main() -> int:
         return 0
 
     if args.only is not None:
-        return only_workload(attn, W, dev, args.only, args.steps, args.warmup)
+        return only_workload(attn, W, dev, args.only, args.steps, args.warmup, args.inputs)
 
     # -- forward headline workload (4 x 16 heads, N = 4096, d = 128, causal) --
     wf = W.WORKLOADS[FWD_WORKLOAD]
