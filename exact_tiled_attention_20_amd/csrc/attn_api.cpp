@@ -21,7 +21,9 @@ namespace {
 // 0.3.0: Nk is always explicit (no "0 means N" sentinel); zero key rows and
 // zero query rows are valid problems; pointers of empty tensors may be NULL.
 // 0.4.0: fp8 (e4m3) forward.
-constexpr int32_t kVersion = 400;
+// 0.5.0: the backward workspace's two arrays have N rounded up to a multiple
+//        of 4 rows per head.
+constexpr int32_t kVersion = 500;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -135,6 +137,12 @@ int key_band(const attn_params* p, int* lo, int* hi) {
 }
 
 size_t stat_bytes(const attn_params* p) { return (size_t)p->B * p->H * p->N * sizeof(float); }
+// Rows per head of the backward's workspace arrays: N rounded up to a
+// multiple of 4, so that every group of four rows is one aligned 16-byte load.
+int stat_rows(const attn_params* p) { return (p->N + 3) & ~3; }
+size_t ws_stat_bytes(const attn_params* p) {
+  return (size_t)p->B * p->H * stat_rows(p) * sizeof(float);
+}
 
 }  // namespace
 
@@ -217,9 +225,9 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
 
 size_t attn_bwd_workspace_bytes(const attn_params* p) {
   if (check_params(p) != ATTN_OK || bwd_supported(p) != ATTN_OK) return 0;
-  // Two fp32 (B, H, N) arrays, each rounded up to 256 bytes: D_i = dO_i . O_i
-  // and lse_i * log2(e).
-  return 2 * ((stat_bytes(p) + 255) & ~size_t(255));
+  // Two fp32 (B, H, Np) arrays (Np = N rounded up to a multiple of 4), each
+  // rounded up to 256 bytes: D_i = dO_i . O_i and lse_i * log2(e).
+  return 2 * ((ws_stat_bytes(p) + 255) & ~size_t(255));
 }
 
 // validate_only: run every check except those on the workspace, then return
@@ -275,11 +283,12 @@ static attn_status bwd_impl(const attn_params* p, int32_t stage, const void* q, 
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    ((stat_bytes(p) + 255) & ~size_t(255)));
+                                    ((ws_stat_bytes(p) + 255) & ~size_t(255)));
   a.kv_len = p->kv_len;
   a.B = p->B;
   a.H = p->H;
   a.N = p->N;
+  a.Np = stat_rows(p);
   a.Nk = key_rows(p);
   const int mask = key_band(p, &a.band_lo, &a.band_hi);
   a.scale = p->scale;

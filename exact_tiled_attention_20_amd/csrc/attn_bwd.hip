@@ -46,16 +46,23 @@ __device__ __forceinline__ float load_out(const void* p, size_t idx) {
 // D_i = sum_c dO[i][c] * O[i][c], and lse_i in log2 units (the form the
 // dK/dV kernel subtracts from its exponents; +inf for a row without visible
 // keys, so that its probabilities come out 0). D/8 lanes per row, 8 elements
-// per lane.
+// per lane. Both arrays have Np rows per head (N rounded up to a multiple of
+// 4); the rows past N hold D = 0 and lse = +inf (finite products, zero
+// probabilities), so that the dK/dV kernel reads every group of four rows as
+// one aligned 16-byte load.
 template <typename E, int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs a) {
   constexpr int LPR = D / 8;  // lanes per row
-  const long long rows = (long long)a.B * a.H * a.N;
+  const long long rows = (long long)a.B * a.H * a.Np;
   const long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / LPR;
   const int part = threadIdx.x % LPR;
+  const long long bh = row / a.Np;
+  const int i = (int)(row - bh * a.Np);
+  const long long src = bh * a.N + i;  // the row in (B, H, N) arrays
+  const bool real = row < rows && i < a.N;
   float acc = 0.f;
-  if (row < rows) {
-    const size_t base = (size_t)row * D + part * 8;
+  if (real) {
+    const size_t base = (size_t)src * D + part * 8;
     const u32x4 g = *(const u32x4*)(a.d_o + base);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -69,7 +76,7 @@ __global__ __launch_bounds__(256) void attn_bwd_preprocess_kernel(const BwdArgs 
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (row < rows && part == 0) {
     a.delta[row] = acc;
-    const float x = a.lse[row];
+    const float x = real ? a.lse[src] : -INFINITY;
     a.lse2[row] = (x == -INFINITY) ? INFINITY : x * kLog2e;
   }
 }
@@ -163,8 +170,8 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   const uint16_t* __restrict__ K = a.k + khead;
   const uint16_t* __restrict__ V = a.v + khead;
   const uint16_t* __restrict__ dO = a.d_o + head;
-  const float* __restrict__ LSE = a.lse2 + (size_t)bh * N;  // lse * log2(e)
-  const float* __restrict__ DEL = a.delta + (size_t)bh * N;
+  const float* __restrict__ LSE = a.lse2 + (size_t)bh * a.Np;  // lse * log2(e)
+  const float* __restrict__ DEL = a.delta + (size_t)bh * a.Np;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -219,7 +226,7 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     TilePairLoader<D, BQ, QW> loader;
     if (w < QW) loader.init(w, lane);
     auto issue_tile = [&](int t, int buf) {
-      if (w < QW)
+      if ((DBUF && QW == NW) || w < QW)
         loader.issue(Q, dO, t * BQ, N, qb0 + buf * TILE_BYTES, ob0 + buf * TILE_BYTES);
     };
 
@@ -241,40 +248,80 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     const float c2 = a.scale_log2;
 
     if (qt0 < nqt) issue_tile(qt0, 0);
+    // lse (in log2 units) and D of this lane's 16 query rows of tile t, rows
+    // t BQ + 8 g4 + 4 hh + e. With double-buffered tiles they are loaded one
+    // tile ahead, at the end of the previous tile's work: loaded at the top of
+    // their own tile, their L2 latency, and with it the wait for the copy of
+    // the next Q / dO tile issued in between (vector-memory operations
+    // complete in issue order), fell between the S / dP products and the
+    // gradient. The workspace rows are padded to a multiple of 4 (the padding
+    // holds finite values), so a group of four rows is always one aligned
+    // 16-byte load, clamped into the padded range for the tail tile.
+    f32x4 lsn[4], dln[4];
+    auto load_rows = [&](int t) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int q4 = min(t * BQ + 8 * g4 + 4 * hh, a.Np - 4);
+        lsn[g4] = *(const f32x4*)(LSE + q4);
+        dln[g4] = *(const f32x4*)(DEL + q4);
+      }
+    };
+    // The waits below count vector-memory operations: per tile a wave issues
+    // exactly the two slices of the next tile's copy, then, at the end, the
+    // eight row loads of the next tile.
+    static_assert(!DBUF || (QW == NW && TilePairLoader<D, BQ, QW>::SPW == 1),
+                  "one Q and one dO slice per wave and tile");
+    if constexpr (DBUF) load_rows(qt0);
     // Unrolled by two (one instantiation per buffer), so LDS addresses carry
     // the buffer offset as an immediate.
     auto tile_step = [&](int t, auto buf_c) {
       constexpr int buf = DBUF ? decltype(buf_c)::value : 0;
-      wait_all_memory();
-      __syncthreads();
       if constexpr (DBUF) {
-        if (t + 1 < nqt) issue_tile(t + 1, buf ^ 1);
+        // Everything but this tile's eight row loads has completed (among it
+        // the copy of this tile); then the copy of the next tile is issued
+        // (the last tile copies itself again into the idle buffer, so that
+        // every tile issues the same operations).
+        wait_vm_lgkm0<8>();
+        barrier_only();
+        issue_tile(min(t + 1, nqt - 1), buf ^ 1);
+      } else {
+        wait_all_memory();
+        __syncthreads();
       }
       const int qbase = t * BQ;
       const bool active = wave_has_keys &&
                           (!BAND || (qbase + 31 >= kw - band_hi &&
                                      (!LO || qbase <= kw + 31 - band_lo)));
-      if (!active) return;
+      if (!active) {
+        if constexpr (DBUF) load_rows(min(t + 1, nqt - 1));
+        return;
+      }
       const char* qb = qb0 + buf * TILE_BYTES;
       const char* ob = ob0 + buf * TILE_BYTES;
 
-      // lse (in log2 units) and D of this lane's 16 query rows
-      // qbase + 8 g4 + 4 hh + e.
-      // Vector loads only where the rows are 16-byte aligned (N % 4 == 0).
       f32x4 ls4[4], dl4[4];
-      const bool vec_rows = (N & 3) == 0;
+      if constexpr (DBUF) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int q4 = qbase + 8 * g4 + 4 * hh;
-        if (vec_rows && q4 + 3 < N) {
-          ls4[g4] = *(const f32x4*)(LSE + q4);
-          dl4[g4] = *(const f32x4*)(DEL + q4);
-        } else {
+        for (int g4 = 0; g4 < 4; ++g4) {
+          ls4[g4] = lsn[g4];
+          dl4[g4] = dln[g4];
+        }
+      } else {
+        // Vector loads only where the rows are 16-byte aligned (N % 4 == 0).
+        const bool vec_rows = (N & 3) == 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int qc = min(q4 + e, N - 1);
-            ls4[g4][e] = LSE[qc];
-            dl4[g4][e] = DEL[qc];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int q4 = qbase + 8 * g4 + 4 * hh;
+          if (vec_rows && q4 + 3 < N) {
+            ls4[g4] = *(const f32x4*)(LSE + q4);
+            dl4[g4] = *(const f32x4*)(DEL + q4);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int qc = min(q4 + e, N - 1);
+              ls4[g4][e] = LSE[qc];
+              dl4[g4][e] = DEL[qc];
+            }
           }
         }
       }
@@ -312,6 +359,9 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
         }
       }
 
+      // The row loads are complete once only the two copy slices issued at
+      // the top may still be outstanding.
+      if constexpr (DBUF) wait_vm<2>();
       // P (masked), dropout, dS; packed as MFMA A operands for 16-query steps.
       // Register r holds query qbase + 8(r/4) + 4hh + r%4.
       const bool need_mask =
@@ -374,12 +424,14 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
           dk[db] = E::mfma(sa[c], u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dk[db]);
         }
       }
+      if constexpr (DBUF) load_rows(min(t + 1, nqt - 1));
     };
     if constexpr (DBUF) {
       for (int t = qt0; t < nqt; t += 2) {
         tile_step(t, std::integral_constant<int, 0>());
         if (t + 1 < nqt) tile_step(t + 1, std::integral_constant<int, 1>());
       }
+      wait_all_memory();  // the last tile's redundant copy and row loads
     } else {
       // One buffer: the next tile is copied once every wave has read this
       // one (waves that skip a tile still meet both barriers).
@@ -421,7 +473,7 @@ static hipError_t launch_all(int stage, const BwdArgs& a, hipStream_t stream) {
   // dQ = 0.
   hipError_t e = hipSuccess;
   if ((stage < 0 || stage == 0) && a.N > 0) {
-    const long long rows = (long long)a.B * a.H * a.N;
+    const long long rows = (long long)a.B * a.H * a.Np;
     const long long threads = rows * (D / 8);
     hipLaunchKernelGGL((attn_bwd_preprocess_kernel<E, D, OUT_F32>),
                        dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);

@@ -97,7 +97,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
     if (qi < N) {
       const float x = a.lse[(size_t)bh * N + qi];
       lse2 = (x == -INFINITY) ? INFINITY : x * kLog2e;
-      dlt = a.delta[(size_t)bh * N + qi];
+      dlt = a.delta[(size_t)bh * a.Np + qi];
     }
   }
 

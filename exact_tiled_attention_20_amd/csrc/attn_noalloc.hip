@@ -2,8 +2,8 @@
 // callers that cannot allocate device memory (code under graph capture, tight
 // serving loops, harnesses that forbid hipMalloc).
 //
-// The workspace attn_bwd takes (two float32 (B, H, N) arrays: D_i = dO_i . O_i
-// and lse_i * log2(e)) lives instead in a fixed file-scope device array,
+// The workspace attn_bwd takes (two float32 (B, H, Np) arrays, Np = N rounded
+// up to a multiple of 4: D_i = dO_i . O_i and lse_i * log2(e)) lives instead in a fixed file-scope device array,
 // `scratch`, of kScratchBytes per GPU. Each GPU that runs the library holds its
 // own copy until the process ends. Host code never uses the array's name as
 // a device address: the address is resolved once per device with

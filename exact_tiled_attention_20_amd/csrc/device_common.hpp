@@ -302,6 +302,14 @@ __device__ __forceinline__ WorkItem decode_work_item(int bid, int heads, int nbl
   return {bh, item - bh * nblk, item < total};
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and every LDS / scalar-memory operation has completed.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
 // Workgroup execution barrier that waits for no outstanding memory operation.
 // The memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }

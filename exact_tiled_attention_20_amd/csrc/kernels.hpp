@@ -65,10 +65,11 @@ struct BwdArgs {
   void* dq;              // out dtype
   void* dk;
   void* dv;
-  float* delta;          // workspace: D_i = dO_i . O_i, (B, H, N) fp32
-  float* lse2;           // workspace: lse_i * log2(e) (+inf where lse_i = -inf), (B, H, N) fp32
+  float* delta;          // workspace: D_i = dO_i . O_i, (B, H, Np) fp32
+  float* lse2;           // workspace: lse_i * log2(e) (+inf where lse_i = -inf), (B, H, Np) fp32
   const int32_t* kv_len;
   int B, H, N;           // N: query rows
+  int Np;                // row stride of delta and lse2: N rounded up to a multiple of 4
   int Nk;                // key/value rows
   int band_lo, band_hi;  // as in FwdArgs
   float scale;

@@ -140,8 +140,10 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k,
                      const void* v, void* o, float* lse, void* stream);
 
 /* Size in bytes of the workspace attn_bwd needs for these parameters:
- * two float32 (B,H,N) arrays (D_i = dO_i . O_i and lse_i * log2(e)), each
- * rounded up to 256 bytes; 0 if the parameters are invalid or N = 0.
+ * two float32 (B,H,Np) arrays (D_i = dO_i . O_i and lse_i * log2(e); Np = N
+ * rounded up to a multiple of 4), each rounded up to 256 bytes; 0 if the
+ * parameters are invalid or N = 0. Callers size the workspace with this
+ * function, not with a formula of their own (the layout changed in 0.5.0).
  * (The backward's row statistics: "Why FlashAttention Is a Kernel Story",
  * section "When it falls down", recomputation from the stored output and
  * log-sum-exp.) */
@@ -226,7 +228,8 @@ attn_status attn_bwd_noalloc(const attn_params* p, const void* q, const void* k,
  * attn_bwd_workspace_bytes). */
 size_t attn_bwd_noalloc_max_workspace_bytes(void);
 
-/* Library version as major*10000 + minor*100 + patch (0.3.0: Nk explicit; 0.4.0: fp8 forward). */
+/* Library version as major*10000 + minor*100 + patch (0.3.0: Nk explicit;
+ * 0.4.0: fp8 forward; 0.5.0: backward workspace rows padded to a multiple of 4). */
 int32_t attn_version(void);
 
 #ifdef __cplusplus

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_version() == 400
+    assert lib.attn_version() == 500
     for code, name in attn.STATUS_NAMES.items():
         assert attn.status_string(code).startswith(name)
     assert "unknown" in attn.status_string(99)
@@ -201,6 +201,15 @@ def test_aliasing_checks_cover_the_key_rows(lib):
     ptrs = _ptrs(10)
     ptrs[7] = ptrs[1] + 2 * 3 * 500 * 64 * 2          # dk inside k's key rows
     assert _bwd(lib, p, ptrs) == 1
+
+
+def test_workspace_rows_are_padded_to_four(lib):
+    """The backward workspace holds two fp32 arrays of B x H x Np rows, Np = N
+    rounded up to a multiple of 4, each rounded up to 256 bytes."""
+    for n, n_pad in ((1, 4), (3, 4), (4, 4), (101, 104), (1000, 1000), (1001, 1004)):
+        p = _params(N=n)
+        want = 2 * (((2 * 3 * n_pad * 4 + 255) // 256) * 256)
+        assert lib.attn_bwd_workspace_bytes(ctypes.byref(p)) == want, n
 
 
 def test_head_dim_256_is_supported(lib):
