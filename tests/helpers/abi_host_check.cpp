@@ -88,7 +88,7 @@ static attn_status bwd(const attn_params& p, size_t ws = (size_t)1 << 30, int st
 int main() {
   using namespace attn;
   // Version and status strings.
-  CHECK(attn_version() == 400);
+  CHECK(attn_version() == 500);
   for (int s = 0; s <= 5; ++s) CHECK(attn_status_string((attn_status)s) != nullptr);
 
   // Invalid fields: nothing is launched.
@@ -164,6 +164,17 @@ int main() {
     CHECK(g_bwd.seed_lo == 0x89ABCDEFu && g_bwd.seed_hi == 0x01234567u);
     CHECK(g_bwd.delta == (float*)fake(9));
     CHECK((char*)g_bwd.lse2 == (char*)fake(9) + (2 * 3 * 100 * 4 + 255) / 256 * 256);
+    CHECK(g_bwd.N == 100 && g_bwd.Np == 100);
+    // Workspace rows are padded to a multiple of 4: N = 101 has 104 per head.
+    {
+      attn_params r = p;
+      r.N = 101;
+      r.Nk = 300;
+      const size_t arr = (2 * 3 * 104 * 4 + 255) / 256 * 256;
+      CHECK(attn_bwd_workspace_bytes(&r) == 2 * arr);
+      CHECK(bwd(r, 2 * arr) == ATTN_OK && g_bwd.N == 101 && g_bwd.Np == 104);
+      CHECK((char*)g_bwd.lse2 == (char*)fake(9) + arr);
+    }
     for (int st = 0; st < 3; ++st) CHECK(bwd(p, (size_t)1 << 30, st) == ATTN_OK && g_stage == st);
     CHECK(bwd(p, (size_t)1 << 30, 3) == ATTN_ERR_INVALID_ARG);
     // Huge window sides are clamped inside the band arithmetic.
