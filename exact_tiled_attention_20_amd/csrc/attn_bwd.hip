@@ -15,7 +15,7 @@
 //      waves per SIMD; 128 keys and 4 waves at d = 64 and d = 256). K and V
 //      rows stay in LDS for the whole pass; Q and dO stream
 //      through LDS in tiles of 32 queries; lse and D come from L2 into
-//      registers. Scores are computed as S = Q K^T so that each lane owns one
+//      registers, one tile ahead. Scores are computed as S = Q K^T so that each lane owns one
 //      key and the query index runs along the accumulator registers: the fp32
 //      registers of P and dS, rounded to the input dtype, are then directly the
 //      A operands of dV = P^T dO and dK = dS^T Q, and dO and Q are fed as B
@@ -119,7 +119,8 @@ __device__ __forceinline__ u32x4 quad_transpose4(u32x4 x, bool b, bool c) {
 // two waves per SIMD. The workgroup's K and V rows stay in LDS for the whole
 // pass; Q and dO tiles of 32 query rows stream HBM -> LDS directly,
 // double-buffered (for d = 128 that fills the 160 KiB of LDS exactly); lse and
-// D of the tile's rows are read from L2 into registers.
+// D of the tile's rows are read from L2 into registers one tile ahead (at d =
+// 256, with single-buffered tiles, at the top of their own tile).
 constexpr int kDkdvWaves = 8;
 // d = 64: 4 waves (128 keys, 48 KiB of LDS), so two workgroups share a CU and
 // the short grids of d = 64 layers (a few key blocks per head) spread over

@@ -30,9 +30,9 @@
  *   Layout.  Q, O, dO, dQ are dense row-major (B, H, N, d) arrays: element
  *            (b, h, i, c) sits at ((b*H + h)*N + i)*d + c. K, V, dK, dV are
  *            (B, H, Nk, d) in the same layout (Nk = N for self-attention,
- *            Nk != N for cross-attention on a non-square grid). lse and the
- *            backward's D are
- *            (B, H, N) float32.
+ *            Nk != N for cross-attention on a non-square grid). lse is
+ *            (B, H, N) float32 (the backward's D lives in its workspace,
+ *            see attn_bwd_workspace_bytes).
  *   Masks.   Query i lines up with key c_i = i + Nk - N (the last query with
  *            the last key; c_i = i when Nk = N). Every set mask must keep a
  *            key for it to be visible:
